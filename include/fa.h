@@ -1,0 +1,113 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward library.
+ *
+ * The library (libfa.so) computes scaled dot-product attention
+ *
+ *     O   = softmax(scale * Q K^T  [+ causal mask]) V
+ *     LSE = log(sum_j exp(scale * q_i . k_j))      (natural log, visible j)
+ *
+ * with an online softmax over streamed K/V tiles, so the Lq x Lk score matrix
+ * never reaches device memory.  Definitions: "Triton Ascend Attention",
+ * section "standard attention computation flow" (scaled scores, row softmax,
+ * weighted sum) and section "Flash Attention optimisation strategy / online
+ * softmax"; the FlashAttention-2 forward article (wsisp.com): the host wrapper
+ * (Q/K/V as [B, H, L, D] tensors, output allocated like Q, a [B, H, Lq] fp32
+ * row statistic), the kernel epilogue (stores m + log(l)) and _attn_fwd_inner
+ * (K/V streamed in blocks, causal predicate offs_m >= offs_n).
+ *
+ * All entry points are plain C; no C++ or framework types cross this line.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o (one type for all four). */
+enum fa_dtype {
+    FA_F32 = 0,  /* IEEE binary32 */
+    FA_F16 = 1,  /* IEEE binary16 */
+    FA_BF16 = 2  /* bfloat16 */
+};
+
+/* Return codes.  FA_OK is zero; every error is positive. */
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* q, k, v or o is NULL */
+    FA_ERR_SHAPE = 2,     /* B, H, Lq or Lk < 1, or a size past the limits */
+    FA_ERR_HEAD_DIM = 3,  /* D is not 64 or 128 */
+    FA_ERR_DTYPE = 4,     /* dtype is not one of enum fa_dtype */
+    FA_ERR_SCALE = 5,     /* scale is NaN or infinite */
+    FA_ERR_ALIGN = 6,     /* q, k, v, o not 16-byte aligned, lse not 4-byte */
+    FA_ERR_ALIAS = 7,     /* o or lse overlaps an input, or o overlaps lse */
+    FA_ERR_POINTER = 8,   /* a pointer is not device memory of this device */
+    FA_ERR_LAUNCH = 9     /* the HIP runtime rejected the kernel launch */
+};
+
+/* Size limits checked by fa_fwd (FA_ERR_SHAPE past them). */
+#define FA_MAX_SEQ  (1LL << 24)   /* Lq, Lk <= 16,777,216 */
+#define FA_MAX_HEADS (1LL << 24)  /* B * H  <= 16,777,216 */
+
+/*
+ * fa_fwd -- attention forward on one GPU, enqueued on `stream`.
+ *
+ * q    [B, H, Lq, D]  device pointer, contiguous row-major (D fastest).
+ * k    [B, H, Lk, D]  device pointer, contiguous row-major.
+ * v    [B, H, Lk, D]  device pointer, contiguous row-major.
+ * o    [B, H, Lq, D]  device pointer, written; same element type as q.
+ * lse  [B, H, Lq]     device pointer to fp32, written at (b*H + h)*Lq + i;
+ *                     may be NULL, then the row statistic is not stored.
+ * B, H         batch and heads (the kernel grid runs over both, as in the
+ *              article's launch grid of query blocks x batch*heads).
+ * Lq, Lk       query and key lengths; independent (cross-attention).
+ * D            head dimension, 64 or 128.
+ * causal       nonzero: query i sees key j only when j <= i (diagonal kept,
+ *              indices counted from the top-left corner, also when Lq != Lk).
+ * scale        multiplies Q K^T; any finite value (the article's host wrapper
+ *              passes 1/sqrt(D); the caller decides here).
+ * dtype        enum fa_dtype of q, k, v, o.
+ * stream       a hipStream_t; NULL is the null stream of the current device.
+ *
+ * Semantics: for each (b, h, i), with J_i the visible keys,
+ *   o[b,h,i,:] = sum_{j in J_i} p_ij v[b,h,j,:],
+ *   p_ij = exp(s_ij - m_i) / l_i,  s_ij = scale * q[b,h,i,:] . k[b,h,j,:],
+ *   lse[b,h,i] = m_i + log(l_i).
+ * bf16/fp16 inputs are multiplied exactly and accumulated in fp32; the
+ * softmax runs in fp32; o is rounded to nearest-even into the I/O type.
+ *
+ * Ownership: the caller owns every buffer; the library allocates nothing,
+ * keeps no state between calls and may be called from several threads.
+ * o and lse must not overlap q, k, v or each other.
+ *
+ * Errors: every check runs on the host before anything is enqueued; on an
+ * error nothing is written and nothing is launched.  The launch itself is
+ * asynchronous: a device fault appears at the caller's next synchronisation.
+ * Returns FA_OK or an enum fa_status code.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+           int causal, float scale, int dtype, void *stream);
+
+/* Static text for a status code ("unknown status" for anything else). */
+const char *fa_status_string(int status);
+
+/*
+ * fa_kernel_name -- name of the kernel fa_fwd would launch for these
+ * arguments (a static string), or NULL when fa_fwd would reject the shape,
+ * head dimension, dtype or scale.  Pure host logic: touches no device.
+ * Used to label measurements and to match profiler output.
+ */
+const char *fa_kernel_name(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                           int64_t D, int causal, float scale, int dtype);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

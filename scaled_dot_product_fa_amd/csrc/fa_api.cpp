@@ -1,0 +1,176 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument validation and
+// kernel dispatch.  Every check runs on the host before anything is enqueued.
+//
+// The checks play the role of the asserts in the FlashAttention-2 forward
+// article's host wrapper (inputs must be device tensors; shapes read from
+// [B, H, L, D]); the output and the [B, H, Lq] fp32 row statistic are
+// allocated by the caller, as the wrapper allocates them before its launch.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+bool overlaps(const void *a, int64_t an, const void *b, int64_t bn)
+{
+    if (a == nullptr || b == nullptr || an <= 0 || bn <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
+}
+
+// Shape, head dimension, dtype and scale checks (pure host logic).
+int check_args(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, float scale,
+               int dtype)
+{
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+    if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
+    if (Lq > FA_MAX_SEQ || Lk > FA_MAX_SEQ || B > FA_MAX_HEADS || H > FA_MAX_HEADS ||
+        B * H > FA_MAX_HEADS)
+        return FA_ERR_SHAPE;
+    // grid size: B*H*ceil(Lq/32) workgroups must fit a 31-bit launch
+    if (B * H * ((Lq + 31) / 32) > (int64_t)0x7fffffff) return FA_ERR_SHAPE;
+    if (!isfinite(scale)) return FA_ERR_SCALE;
+    return FA_OK;
+}
+
+// Device memory of the current device (or managed memory)?
+bool is_device_ptr(const void *p, int device)
+{
+    hipPointerAttribute_t attr;
+    memset(&attr, 0, sizeof(attr));
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();  // do not leave a stale error behind
+        return false;
+    }
+    if (attr.type == hipMemoryTypeManaged) return true;
+    return attr.type == hipMemoryTypeDevice && attr.device == device;
+}
+
+fa::FwdArgs make_args(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, int causal,
+                      float scale, int dtype, void *stream)
+{
+    fa::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.B = B;
+    a.H = H;
+    a.Lq = Lq;
+    a.Lk = Lk;
+    a.D = D;
+    a.causal = causal ? 1 : 0;
+    a.scale = scale;
+    a.dtype = dtype;
+    a.stream = static_cast<hipStream_t>(stream);
+    return a;
+}
+
+// Tuning override "NWxQBxBN" (for sweeps), or "valu" to force the vector-ALU
+// kernel.  Unset means the built-in choice.
+bool env_tile(fa::MfmaTile &t, bool &force_valu)
+{
+    force_valu = false;
+    const char *s = getenv("FA_TILE");
+    if (s == nullptr || *s == '\0') return false;
+    if (strcmp(s, "valu") == 0) {
+        force_valu = true;
+        return false;
+    }
+    int nw = 0, qb = 0, bn = 0;
+    char x1 = 0, x2 = 0;
+    char tail = 0;
+    const int n = sscanf(s, "%d%c%d%c%d%c", &nw, &x1, &qb, &x2, &bn, &tail);
+    if (n != 5 || x1 != 'x' || x2 != 'x') return false;
+    t = fa::MfmaTile{nw, qb, bn};
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+           int64_t H, int64_t Lq, int64_t Lk, int64_t D, int causal, float scale, int dtype,
+           void *stream)
+{
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULL;
+    int rc = check_args(B, H, Lq, Lk, D, scale, dtype);
+    if (rc != FA_OK) return rc;
+
+    const int64_t es = dtype == FA_F32 ? 4 : 2;
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o);
+    if ((mis & 15u) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_ALIGN;
+
+    const int64_t nq = B * H * Lq * D * es, nk = B * H * Lk * D * es, nl = B * H * Lq * 4;
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nk) || overlaps(o, nq, v, nk) ||
+        overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nk) ||
+        overlaps(lse, nl, o, nq))
+        return FA_ERR_ALIAS;
+
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) {
+        (void)hipGetLastError();
+        return FA_ERR_POINTER;
+    }
+    if (!is_device_ptr(q, device) || !is_device_ptr(k, device) || !is_device_ptr(v, device) ||
+        !is_device_ptr(o, device) || (lse != nullptr && !is_device_ptr(lse, device)))
+        return FA_ERR_POINTER;
+
+    const fa::FwdArgs a = make_args(q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, dtype,
+                                    stream);
+    fa::MfmaTile tile{};
+    bool force_valu = false;
+    const bool have_tile = env_tile(tile, force_valu);
+    hipError_t e;
+    if (!force_valu && fa::mfma_supported(a))
+        e = fa::mfma_launch(a, have_tile ? tile : fa::mfma_choose_tile(a));
+    else
+        e = fa::valu_launch(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+const char *fa_status_string(int status)
+{
+    switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "q, k, v or o is NULL";
+    case FA_ERR_SHAPE: return "B, H, Lq or Lk out of range";
+    case FA_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
+    case FA_ERR_DTYPE: return "dtype must be FA_F32, FA_F16 or FA_BF16";
+    case FA_ERR_SCALE: return "scale must be finite";
+    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA_ERR_POINTER: return "a pointer is not device memory of the current device";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char *fa_kernel_name(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                           int causal, float scale, int dtype)
+{
+    if (check_args(B, H, Lq, Lk, D, scale, dtype) != FA_OK) return nullptr;
+    const fa::FwdArgs a = make_args(nullptr, nullptr, nullptr, nullptr, nullptr, B, H, Lq, Lk,
+                                    D, causal, scale, dtype, nullptr);
+    fa::MfmaTile tile{};
+    bool force_valu = false;
+    const bool have_tile = env_tile(tile, force_valu);
+    if (!force_valu && fa::mfma_supported(a))
+        return fa::mfma_kernel_name(a, have_tile ? tile : fa::mfma_choose_tile(a));
+    return fa::valu_kernel_name(a);
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

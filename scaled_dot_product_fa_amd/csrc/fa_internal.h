@@ -1,0 +1,39 @@
+// fa_internal.h -- declarations shared by the library's host and kernel
+// sources.  Not installed; the public interface is include/fa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Arguments of one forward call after validation.
+struct FwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int64_t B, H, Lq, Lk, D;
+    int causal;
+    float scale;
+    int dtype;
+    hipStream_t stream;
+};
+
+// Tile shape of the MFMA kernel: NW waves per workgroup, each wave owning
+// QB blocks of 32 queries (so BM = NW * QB * 32 query rows per workgroup),
+// and BN keys per K/V tile.
+struct MfmaTile {
+    int nw, qb, bn;
+};
+
+// MFMA kernel: fp16/bf16 I/O, D in {64, 128}, scale > 0.
+bool mfma_supported(const FwdArgs &a);
+MfmaTile mfma_choose_tile(const FwdArgs &a);
+const char *mfma_kernel_name(const FwdArgs &a, const MfmaTile &t);
+hipError_t mfma_launch(const FwdArgs &a, const MfmaTile &t);
+
+// Vector-ALU kernel: any I/O type, D in {64, 128}, any finite scale.
+const char *valu_kernel_name(const FwdArgs &a);
+hipError_t valu_launch(const FwdArgs &a);
+
+}  // namespace fa

@@ -1,0 +1,494 @@
+// fa_mfma.hip -- FlashAttention-2 forward for gfx950 on bf16/fp16 MFMA.
+//
+// Method (FlashAttention-2 forward article, wsisp.com: host wrapper, launch
+// grid, fwd_flash_attn_kernel and _attn_fwd_inner; "Triton Ascend Attention",
+// online softmax section): one workgroup per block of BM query rows of one
+// (batch, head); K/V stream through LDS in tiles of BN keys; per query row a
+// running max m, running sum l and an unnormalised fp32 accumulator are
+// updated per tile with the rescale factor alpha = exp(m_old - m_new); the
+// output is divided by l once at the end and m + log(l) is stored.  Causal
+// tiles beyond the block's diagonal are never loaded, and only tiles that
+// straddle the diagonal (or the ragged end of the keys) are masked, keeping
+// key j for query i when j <= i ("flash-attention-kernel" skill page).
+//
+// gfx950 mapping (our design, not the article's):
+//   * Scores are computed transposed, S^T = K Q^T, on
+//     v_mfma_f32_32x32x16_{bf16,f16}: A = 32 keys x 16 dims from LDS,
+//     B = 16 dims x 32 queries held in VGPRs for the whole kernel.  In the
+//     32x32 accumulator every lane then owns one query column, so the row max
+//     and row sum are in-lane reductions plus one exchange between the two
+//     32-lane halves (v_permlane32_swap).
+//   * The K rows feeding A are read in a permuted order (bits 2 and 3 of the
+//     row index swapped) so that each lane's 16 accumulator values are 2 runs
+//     of 8 consecutive keys.  The probabilities, rounded to the I/O type,
+//     are then directly the B operand of O^T += V^T P^T (again
+//     32x32x16), with no data movement between lanes.
+//   * V is transposed while it is staged into LDS (V^T, keys fastest), so the
+//     A operand of the PV product is one 16-byte LDS read per lane.
+//   * Both LDS tiles use XOR swizzles so the 16-byte reads of a wave hit
+//     distinct banks.  Tiles are double-buffered: the global loads of tile
+//     j+1 are issued before the math of tile j and written to the other LDS
+//     buffer after it, one barrier per tile.
+//   * exp2 is used with c = scale*log2(e) folded into one FMA per score:
+//     p = exp2(s*c - m*c).  The stabiliser m only moves when the tile max
+//     exceeds it by more than kLazyThreshold (log2 units), so the fp32
+//     accumulator is rescaled rarely; the softmax is unchanged by the choice
+//     of stabiliser (both l and the accumulator use the same one) and p stays
+//     below 2^kLazyThreshold.
+//   * Workgroup ids are remapped so one head's query blocks run on one XCD
+//     (shared L2), and causal grids start with the longest blocks.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+// The running max is only raised when it grew by more than this many binary
+// orders of magnitude; until then probabilities may reach 2^kLazyThreshold.
+constexpr float kLazyThreshold = 8.0f;
+
+struct Bf16Ops {
+    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    // two floats -> one dword, round to nearest even, first value low
+    static __device__ __forceinline__ uint32_t pack2(float x, float y)
+    {
+        bf16x2 r = {(__bf16)x, (__bf16)y};
+        return __builtin_bit_cast(uint32_t, r);
+    }
+};
+
+struct F16Ops {
+    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float x, float y)
+    {
+        f16x2 r = {(_Float16)x, (_Float16)y};
+        return __builtin_bit_cast(uint32_t, r);
+    }
+};
+
+// Exchange between lane l and lane l ^ 32, combined with op.  With both
+// operands equal, v_permlane32_swap leaves one copy of each half in each
+// result, so op(r0, r1) is op(x[l % 32], x[l % 32 + 32]) in every lane.
+__device__ __forceinline__ float half_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                              false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                              false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Swap bits 2 and 3 of a row index within a 32-row key block.
+__device__ __forceinline__ int swap_bits23(int r)
+{
+    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+struct Params {
+    const uint16_t *q, *k, *v;
+    uint16_t *o;
+    float *lse;
+    int BH, Lq, Lk, ntq;
+    float scale, c;  // c = scale * log2(e)
+};
+
+// Workgroup id -> (head bh, query block qt).  Hardware places workgroup w
+// on XCD w % 8; consecutive logical ids are made to share an XCD.
+__device__ __forceinline__ void decompose(int wg, int nwg, int BH, int ntq,
+                                          bool causal, int &bh, int &qt)
+{
+    const int per = nwg >> 3, rem = nwg & 7;
+    const int xcd = wg & 7, idx = wg >> 3;
+    if (causal && (BH & 7) == 0) {
+        // each XCD owns BH/8 heads; longest query blocks first
+        const int hpx = BH >> 3;
+        qt = ntq - 1 - idx / hpx;
+        bh = xcd * hpx + idx % hpx;
+        return;
+    }
+    const int logical = xcd < rem ? xcd * (per + 1) + idx
+                                  : rem * (per + 1) + (xcd - rem) * per + idx;
+    bh = logical / ntq;
+    qt = logical % ntq;
+    if (causal) qt = ntq - 1 - qt;
+}
+
+template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN>
+__global__ __launch_bounds__(NW * 64) void fa_fwd_mfma_kernel(Params p)
+{
+    constexpr int NT = NW * 64;          // threads
+    constexpr int BM = NW * QB * 32;     // query rows per workgroup
+    constexpr int DC = D / 16;           // 16-dim chunks (k of the QK^T MFMA)
+    constexpr int DB = D / 32;           // 32-dim blocks (rows of O^T)
+    constexpr int KB = BN / 32;          // 32-key blocks (rows of S^T)
+    constexpr int KC = BN / 16;          // 16-key chunks (k of the PV MFMA)
+    constexpr int KROW = D * 2;          // bytes per K row in LDS
+    constexpr int VROW = BN * 2;         // bytes per V^T row in LDS
+    constexpr int KCH = D / 8;           // 16-byte chunks per K row
+    constexpr int VCH = BN / 8;          // 16-byte chunks per V^T row
+    constexpr int KBYTES = BN * KROW;
+    constexpr int VBYTES = D * VROW;
+    constexpr int BUF = KBYTES + VBYTES;
+    constexpr int K_PER_T = BN * KCH / NT;       // K chunks loaded per thread
+    constexpr int V_KEYS = BN * (D / 8) / NT;    // keys per thread in the V load
+    static_assert(K_PER_T >= 1 && BN * KCH % NT == 0, "K tile split");
+    static_assert(V_KEYS == 2 || V_KEYS == 4 || V_KEYS == 8, "V tile split");
+    static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    int bh, qt;
+    decompose(blockIdx.x, gridDim.x, p.BH, p.ntq, CAUSAL, bh, qt);
+    const int q_first = qt * BM;
+    const int qw = q_first + wave * QB * 32;  // first query row of this wave
+
+    const uint16_t *qh = p.q + (int64_t)bh * p.Lq * D;
+    const uint16_t *kh = p.k + (int64_t)bh * p.Lk * D;
+    const uint16_t *vh = p.v + (int64_t)bh * p.Lk * D;
+
+    // ---- Q^T operand, resident in VGPRs: lane holds 8 dims of its query.
+    u32x4 qreg[QB][DC];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const int row = qw + b * 32 + l32;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (row < p.Lq)
+                x = *reinterpret_cast<const u32x4 *>(qh + (uint32_t)row * D + dc * 16 + hi * 8);
+            qreg[b][dc] = x;
+        }
+    }
+
+    f32x16 oacc[DB][QB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][b][i] = 0.f;
+    float m_run[QB], l_part[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        m_run[b] = -INFINITY;
+        l_part[b] = 0.f;
+    }
+
+    const int kv_end = CAUSAL ? min(p.Lk, q_first + BM) : p.Lk;
+    const int ntiles = (kv_end + BN - 1) / BN;
+
+    // ---- global -> register staging of one K/V tile
+    u32x4 kst[K_PER_T];
+    u32x4 vst[V_KEYS];
+    // V load split: thread owns V_KEYS consecutive keys x 8 dims
+    const int v_dc = tid % (D / 8);
+    const int v_kg = tid / (D / 8);
+
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int r = 0; r < K_PER_T; ++r) {
+            const int ci = tid + NT * r;
+            const int row = ci / KCH, c = ci % KCH;
+            const int key = k0 + row;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (key < p.Lk)
+                x = *reinterpret_cast<const u32x4 *>(kh + (uint32_t)key * D + c * 8);
+            kst[r] = x;
+        }
+#pragma unroll
+        for (int r = 0; r < V_KEYS; ++r) {
+            const int key = k0 + v_kg * V_KEYS + r;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (key < p.Lk)
+                x = *reinterpret_cast<const u32x4 *>(vh + (uint32_t)key * D + v_dc * 8);
+            vst[r] = x;
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+        uint8_t *kb = smem + buf * BUF;
+        uint8_t *vb = kb + KBYTES;
+#pragma unroll
+        for (int r = 0; r < K_PER_T; ++r) {
+            const int ci = tid + NT * r;
+            const int row = ci / KCH, c = ci % KCH;
+            const int pc = c ^ (swap_bits23(row & 15) & (KCH - 1));
+            *reinterpret_cast<u32x4 *>(kb + row * KROW + pc * 16) = kst[r];
+        }
+        // transpose V_KEYS keys x 8 dims into 8 rows of V^T
+        const int key0 = v_kg * V_KEYS;
+        const int ch = key0 >> 3;            // 16-byte chunk within the V^T row
+        const int off = (key0 & 7) * 2;      // byte offset within the chunk
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int d = v_dc * 8 + e;
+            const int pc = ch ^ (((d >> 3) ^ d) & (VCH - 1));
+            uint8_t *dst = vb + d * VROW + pc * 16 + off;
+            uint32_t w[V_KEYS / 2];
+#pragma unroll
+            for (int r = 0; r < V_KEYS / 2; ++r) {
+                const uint32_t a = vst[2 * r][e >> 1];
+                const uint32_t b = vst[2 * r + 1][e >> 1];
+                w[r] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u))
+                               : ((a & 0xffffu) | (b << 16));
+            }
+            if constexpr (V_KEYS == 2) {
+                *reinterpret_cast<uint32_t *>(dst) = w[0];
+            } else if constexpr (V_KEYS == 4) {
+                u32x2 x = {w[0], w[1]};
+                *reinterpret_cast<u32x2 *>(dst) = x;
+            } else {
+                u32x4 x = {w[0], w[1], w[2], w[3]};
+                *reinterpret_cast<u32x4 *>(dst) = x;
+            }
+        }
+    };
+
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    const float c = p.c;
+    // K row this lane feeds into the A operand of S^T = K Q^T
+    const int krow_lane = swap_bits23(l32);
+
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        const int k0 = j * BN;
+        const bool has_next = j + 1 < ntiles;
+        if (has_next) load_tile(k0 + BN);
+
+        const bool wave_idle = (qw >= p.Lq) || (CAUSAL && k0 > qw + QB * 32 - 1);
+        if (!wave_idle) {
+            const uint8_t *kb = smem + buf * BUF;
+            const uint8_t *vb = kb + KBYTES;
+
+            // ---- S^T = K Q^T (raw scores, fp32)
+            f32x16 s[KB][QB];
+#pragma unroll
+            for (int kb_i = 0; kb_i < KB; ++kb_i)
+#pragma unroll
+                for (int b = 0; b < QB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s[kb_i][b][i] = 0.f;
+#pragma unroll
+            for (int kb_i = 0; kb_i < KB; ++kb_i) {
+                const int row = kb_i * 32 + krow_lane;
+                const int sw = swap_bits23(row & 15) & (KCH - 1);
+#pragma unroll
+                for (int dc = 0; dc < DC; ++dc) {
+                    const int pc = (dc * 2 + hi) ^ sw;
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(kb + row * KROW + pc * 16);
+#pragma unroll
+                    for (int b = 0; b < QB; ++b) s[kb_i][b] = Ops::mma(a, qreg[b][dc], s[kb_i][b]);
+                }
+            }
+
+            // ---- masking: ragged key end, and the diagonal when causal
+            const bool need_mask = (k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw);
+            if (need_mask) {
+#pragma unroll
+                for (int kb_i = 0; kb_i < KB; ++kb_i)
+#pragma unroll
+                    for (int b = 0; b < QB; ++b)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int key = k0 + kb_i * 32 + (i >> 3) * 16 + hi * 8 + (i & 7);
+                            const int qry = qw + b * 32 + l32;
+                            const bool keep = key < p.Lk && (!CAUSAL || key <= qry);
+                            s[kb_i][b][i] = keep ? s[kb_i][b][i] : -INFINITY;
+                        }
+            }
+
+            // ---- online softmax per query block; P^T packed for the B operand
+            u32x4 pk[KC][QB];
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb_i = 0; kb_i < KB; ++kb_i)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb_i][b][i]);
+                mx = half_max(mx);
+                const float m_new = fmaxf(m_run[b], mx);
+                const bool grow = (m_new - m_run[b]) * c > kLazyThreshold;
+                if (__any(grow)) {
+                    // m_run = -inf gives alpha = 0 (nothing accumulated yet)
+                    const float alpha = (m_new == -INFINITY)
+                                            ? 1.f
+                                            : __builtin_amdgcn_exp2f((m_run[b] - m_new) * c);
+                    m_run[b] = m_new;
+                    l_part[b] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) oacc[db][b][i] *= alpha;
+                }
+                const float mc = (m_run[b] == -INFINITY) ? 0.f : m_run[b] * c;
+                float rs = 0.f;
+#pragma unroll
+                for (int kb_i = 0; kb_i < KB; ++kb_i) {
+                    float e[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        e[i] = __builtin_amdgcn_exp2f(fmaf(s[kb_i][b][i], c, -mc));
+                        rs += e[i];
+                    }
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        u32x4 x;
+#pragma unroll
+                        for (int w = 0; w < 4; ++w)
+                            x[w] = Ops::pack2(e[h * 8 + 2 * w], e[h * 8 + 2 * w + 1]);
+                        pk[kb_i * 2 + h][b] = x;
+                    }
+                }
+                l_part[b] += rs;
+            }
+
+            // ---- O^T += V^T P^T
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int d = db * 32 + l32;
+                const int sw = ((d >> 3) ^ d) & (VCH - 1);
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    const int pc = (kc * 2 + hi) ^ sw;
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(vb + d * VROW + pc * 16);
+#pragma unroll
+                    for (int b = 0; b < QB; ++b) oacc[db][b] = Ops::mma(a, pk[kc][b], oacc[db][b]);
+                }
+            }
+        }
+
+        if (has_next) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = acc / l, rounded to nearest even; LSE = m*scale + ln l
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const float l = half_sum(l_part[b]);
+        const int row = qw + b * 32 + l32;
+        if (row < p.Lq) {
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            uint16_t *orow = p.o + ((int64_t)bh * p.Lq + row) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d = db * 32 + g * 8 + hi * 4;
+                    u32x2 x = {Ops::pack2(oacc[db][b][4 * g] * inv, oacc[db][b][4 * g + 1] * inv),
+                               Ops::pack2(oacc[db][b][4 * g + 2] * inv, oacc[db][b][4 * g + 3] * inv)};
+                    *reinterpret_cast<u32x2 *>(orow + d) = x;
+                }
+            if (p.lse != nullptr && hi == 0)
+                p.lse[(int64_t)bh * p.Lq + row] =
+                    l > 0.f ? m_run[b] * p.scale + __logf(l) : -INFINITY;
+        }
+    }
+}
+
+template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN>
+hipError_t launch_cfg(const FwdArgs &a)
+{
+    constexpr int BM = NW * QB * 32;
+    Params p;
+    p.q = static_cast<const uint16_t *>(a.q);
+    p.k = static_cast<const uint16_t *>(a.k);
+    p.v = static_cast<const uint16_t *>(a.v);
+    p.o = static_cast<uint16_t *>(a.o);
+    p.lse = a.lse;
+    p.BH = (int)(a.B * a.H);
+    p.Lq = (int)a.Lq;
+    p.Lk = (int)a.Lk;
+    p.ntq = (int)((a.Lq + BM - 1) / BM);
+    p.scale = a.scale;
+    p.c = a.scale * kLog2e;
+    const int64_t nwg = (int64_t)p.BH * p.ntq;
+    hipLaunchKernelGGL((fa_fwd_mfma_kernel<Ops, D, CAUSAL, NW, QB, BN>),
+                       dim3((unsigned)nwg), dim3(NW * 64), 0, a.stream, p);
+    return hipGetLastError();
+}
+
+template <typename Ops, int D, bool CAUSAL>
+hipError_t launch_tile(const FwdArgs &a, const MfmaTile &t)
+{
+    if (t.nw == 4 && t.qb == 1 && t.bn == 64) return launch_cfg<Ops, D, CAUSAL, 4, 1, 64>(a);
+    if (t.nw == 4 && t.qb == 2 && t.bn == 64) return launch_cfg<Ops, D, CAUSAL, 4, 2, 64>(a);
+    return hipErrorInvalidConfiguration;
+}
+
+template <typename Ops>
+hipError_t launch_ops(const FwdArgs &a, const MfmaTile &t)
+{
+    if (a.D == 64)
+        return a.causal ? launch_tile<Ops, 64, true>(a, t) : launch_tile<Ops, 64, false>(a, t);
+    return a.causal ? launch_tile<Ops, 128, true>(a, t) : launch_tile<Ops, 128, false>(a, t);
+}
+
+}  // namespace
+
+bool mfma_supported(const FwdArgs &a)
+{
+    return (a.dtype == 1 || a.dtype == 2) && (a.D == 64 || a.D == 128) && a.scale > 0.f;
+}
+
+MfmaTile mfma_choose_tile(const FwdArgs &a)
+{
+    (void)a;
+    return MfmaTile{4, 1, 64};
+}
+
+const char *mfma_kernel_name(const FwdArgs &a, const MfmaTile &t)
+{
+    (void)t;
+    static const char *names[2][2][2] = {
+        {{"fa_fwd_mfma_f16_d64", "fa_fwd_mfma_f16_d64_causal"},
+         {"fa_fwd_mfma_f16_d128", "fa_fwd_mfma_f16_d128_causal"}},
+        {{"fa_fwd_mfma_bf16_d64", "fa_fwd_mfma_bf16_d64_causal"},
+         {"fa_fwd_mfma_bf16_d128", "fa_fwd_mfma_bf16_d128_causal"}},
+    };
+    return names[a.dtype == 2][a.D == 128][a.causal ? 1 : 0];
+}
+
+hipError_t mfma_launch(const FwdArgs &a, const MfmaTile &t)
+{
+    return a.dtype == 2 ? launch_ops<Bf16Ops>(a, t) : launch_ops<F16Ops>(a, t);
+}
+
+}  // namespace fa

@@ -19,3 +19,14 @@ def pytest_configure(config):
 def oracle_lib():
     import oracle
     return oracle.load()
+
+
+def pytest_collection_modifyitems(config, items):
+    gpu_items = [it for it in items if "gpu" in it.keywords]
+    if not gpu_items:
+        return
+    import torch
+    if not torch.cuda.is_available():
+        skip = pytest.mark.skip(reason="no GPU visible in this process")
+        for it in gpu_items:
+            it.add_marker(skip)

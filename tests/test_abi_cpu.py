@@ -1,0 +1,131 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol that
+include/fa.h declares, and rejects bad arguments on the host before any
+launch (fake addresses are never dereferenced because validation fails
+first)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import scaled_dot_product_fa_amd as fa
+from scaled_dot_product_fa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["fa_fwd", "fa_kernel_name",
+                                    "fa_status_string", "fa_version"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(0, 10):
+        s = fa.fa_status_string(code)
+        assert s and s != "unknown status"
+    assert fa.fa_status_string(99) == "unknown status"
+    assert fa.fa_status_string(-1) == "unknown status"
+
+
+def test_enum_values_match_header():
+    text = open(HEADER).read()
+    for name, val in (("FA_F32", 0), ("FA_F16", 1), ("FA_BF16", 2)):
+        assert re.search(rf"\b{name}\s*=\s*{val}\b", text)
+    for code, name in _lib.STATUS.items():
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
+
+
+# Fake, well-separated, 16-byte aligned addresses: validation must reject
+# the call before anything could touch them.
+Q, K, V, O, L = 1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40
+GOOD = dict(B=1, H=2, Lq=128, Lk=128, D=64, causal=0, scale=0.125, dtype=2)
+
+
+def call(q=Q, k=K, v=V, o=O, lse=L, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fa.fa_fwd(q, k, v, o, lse, a["B"], a["H"], a["Lq"], a["Lk"],
+                     a["D"], a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_null_pointer(which):
+    assert call(**{which: None}) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 2), (dict(H=0), 2), (dict(Lq=0), 2), (dict(Lk=0), 2),
+    (dict(B=-3), 2), (dict(Lq=(1 << 24) + 1), 2), (dict(Lk=(1 << 24) + 1), 2),
+    (dict(B=1 << 13, H=1 << 12), 2),
+    (dict(D=32), 3), (dict(D=96), 3), (dict(D=256), 3), (dict(D=0), 3),
+    (dict(dtype=3), 4), (dict(dtype=-1), 4),
+    (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5),
+    (dict(scale=-float("inf")), 5),
+])
+def test_bad_arguments(kw, code):
+    assert call(**kw) == code
+
+
+def test_misaligned_pointers():
+    assert call(q=Q + 8) == 6
+    assert call(o=O + 2) == 6
+    assert call(lse=L + 2) == 6
+
+
+def test_aliasing_rejected():
+    nbytes = 1 * 2 * 128 * 64 * 2
+    assert call(o=Q) == 7                      # o on top of q
+    assert call(o=K + nbytes - 16) == 7        # o overlapping the tail of k
+    assert call(lse=O + 64) == 7               # lse inside o
+    assert call(lse=V) == 7
+
+
+def test_non_device_pointers_rejected_without_gpu():
+    # plain host addresses are not device memory (and there is no GPU here)
+    buf = [ctypes.create_string_buffer(1 << 16) for _ in range(5)]
+    addr = [((ctypes.addressof(b) + 15) // 16) * 16 for b in buf]
+    assert call(q=addr[0], k=addr[1], v=addr[2], o=addr[3], lse=addr[4]) == 8
+
+
+def test_kernel_selection():
+    # bf16/fp16 with a positive scale run on MFMA, everything else on VALU
+    assert fa.fa_kernel_name(4, 16, 4096, 4096, 128, 0, 0.088, 2) == \
+        "fa_fwd_mfma_bf16_d128"
+    assert fa.fa_kernel_name(1, 32, 16384, 16384, 128, 1, 0.088, 2) == \
+        "fa_fwd_mfma_bf16_d128_causal"
+    assert fa.fa_kernel_name(8, 16, 1024, 4000, 64, 0, 0.125, 1) == \
+        "fa_fwd_mfma_f16_d64"
+    assert fa.fa_kernel_name(1, 2, 128, 128, 64, 1, 0.125, 0) == \
+        "fa_fwd_valu_f32_d64_causal"
+    assert fa.fa_kernel_name(1, 2, 128, 128, 64, 0, 0.0, 2) == \
+        "fa_fwd_valu_bf16_d64"
+    assert fa.fa_kernel_name(1, 2, 128, 128, 128, 0, -1.0, 1) == \
+        "fa_fwd_valu_f16_d128"
+    assert fa.fa_kernel_name(1, 2, 128, 128, 65, 0, 1.0, 2) is None
+    assert fa.fa_kernel_name(1, 2, 128, 128, 64, 0, math.nan, 2) is None
+    assert fa.fa_kernel_name(1, 2, 0, 128, 64, 0, 1.0, 2) is None
+
+
+def test_forward_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)
+
+
+def test_version():
+    assert fa.fa_version() >= 100

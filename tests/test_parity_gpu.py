@@ -1,0 +1,244 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Tolerances are the ones the target states: max-abs error on O of 2e-2 for
+bf16/fp16 I/O and 1e-5 for fp32 I/O, and 1e-3 on the natural-log LSE.
+Small shapes are compared element by element over the whole output; the
+five named workloads at full size are compared on sampled rows (all heads;
+rows 0 and 1, tile boundaries, the middle, the last rows and seeded random
+rows), which the oracle computes one by one.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scaled_dot_product_fa_amd as fa
+from scaled_dot_product_fa_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
+TOL_LSE = 1e-3
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to64(t):
+    return t.to(torch.float64).numpy()
+
+
+def gpu_forward(q, k, v, causal, scale):
+    dq, dk, dv = (t.cuda() for t in (q, k, v))
+    o, lse = fa.forward(dq, dk, dv, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def check_full(q, k, v, causal, scale, dtype, label=""):
+    say(f"[parity] {label} q{tuple(q.shape)} k{tuple(k.shape)} {dtype} "
+        f"causal={causal} scale={scale:.6g} "
+        f"kernel={fa.fa_kernel_name(*q.shape[:3], k.shape[2], q.shape[3], int(causal), scale, fa.dtype_code(q.dtype))}")
+    o, lse = gpu_forward(q, k, v, causal, scale)
+    ro, rl = oracle.attention(to64(q), to64(k), to64(v), causal, scale)
+    eo = np.abs(to64(o) - ro).max()
+    el = np.abs(lse.double().numpy() - rl).max()
+    say(f"[parity]   max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert np.isfinite(to64(o)).all() and np.isfinite(lse.numpy()).all()
+    assert eo <= TOL_O[dtype], eo
+    assert el <= TOL_LSE, el
+    return o, lse
+
+
+# ---------------------------------------------------------------- workloads
+
+def _workload_case(name, mode):
+    w = inputs.CONFIGS[name]
+    causal = mode == "causal"
+    q, k, v = inputs.workload_inputs(w)
+    label = f"{name}/{mode}"
+    if w.name == "tiny" or w.name == "small":
+        check_full(q, k, v, causal, w.scale, w.dtype, label)
+        return
+    say(f"[parity] {label} B={w.B} H={w.H} Lq={w.Lq} Lk={w.Lk} D={w.D} "
+        f"{w.dtype} sampled rows, kernel="
+        f"{fa.fa_kernel_name(w.B, w.H, w.Lq, w.Lk, w.D, int(causal), w.scale, fa.dtype_code(q.dtype))}")
+    o, lse = gpu_forward(q, k, v, causal, w.scale)
+    ids = inputs.sample_rows(w.B, w.H, w.Lq, n_random=24, seed=w.seed,
+                             tile=64)
+    ro, rl = oracle.attention_rows(to64(q), to64(k), to64(v), ids.numpy(),
+                                   causal, w.scale)
+    go = to64(o.reshape(-1, w.D)[ids])
+    gl = lse.reshape(-1)[ids].double().numpy()
+    eo, el = np.abs(go - ro).max(), np.abs(gl - rl).max()
+    say(f"[parity]   rows={ids.numel()} max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert np.isfinite(to64(o)).all() and np.isfinite(lse.numpy()).all()
+    assert eo <= TOL_O[w.dtype], eo
+    assert el <= TOL_LSE, el
+
+
+WORKLOAD_CASES = [(n, m) for n, w in inputs.CONFIGS.items() for m in w.modes]
+
+
+@pytest.mark.parametrize("name,mode", WORKLOAD_CASES,
+                         ids=[f"{n}-{m}" for n, m in WORKLOAD_CASES])
+def test_workload(name, mode):
+    _workload_case(name, mode)
+
+
+# ------------------------------------------------- ragged multi-tile shapes
+
+RAGGED = [
+    # B, H, Lq, Lk, D, dtype
+    (1, 3, 333, 517, 128, "bf16"),
+    (2, 2, 257, 190, 64, "f16"),
+    (1, 2, 130, 77, 128, "f32"),
+    (1, 1, 1, 1, 64, "bf16"),
+    (1, 1, 1, 1000, 128, "bf16"),
+    (1, 2, 700, 1, 64, "f16"),
+    (2, 1, 64, 64, 128, "bf16"),
+    (1, 1, 129, 4001, 64, "f16"),
+    (1, 2, 600, 260, 128, "bf16"),   # Lq > Lk, causal rows past Lk see all
+    (3, 1, 95, 97, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=[str(s) for s in RAGGED])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged(shape, causal):
+    B, H, Lq, Lk, D, dt = shape
+    q, k, v = inputs.make_qkv(B, H, Lq, Lk, D, dt, seed=B + H + Lq + Lk + D)
+    check_full(q, k, v, causal, 1.0 / math.sqrt(D), dt, "ragged")
+
+
+@pytest.mark.parametrize("tile", ["4x1x64", "4x2x64", "valu"])
+@pytest.mark.parametrize("D,dt", [(64, "bf16"), (128, "f16")])
+def test_tile_variants(tile, D, dt, monkeypatch):
+    monkeypatch.setenv("FA_TILE", tile)
+    for causal in (False, True):
+        q, k, v = inputs.make_qkv(2, 2, 300, 450, D, dt, seed=D + len(tile))
+        check_full(q, k, v, causal, 0.11, dt, f"tile={tile}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5, 1e-3])
+def test_scale_values(scale):
+    q, k, v = inputs.make_qkv(1, 2, 150, 200, 64, "bf16", seed=11)
+    for causal in (False, True):
+        check_full(q, k, v, causal, scale, "bf16", f"scale={scale}")
+
+
+# ------------------------------------------------------------ closed forms
+
+@pytest.mark.parametrize("Lk", [4000, 4001, 4096])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_q_zero_gives_log_lk(Lk, dt):
+    """Q = 0: every score is 0, so LSE = ln Lk and O is the mean of V
+    (this catches keys past Lk leaking into the sum)."""
+    say(f"[closed] Q=0 Lk={Lk} {dt}")
+    _, k, v = inputs.make_qkv(1, 2, 70, Lk, 64, dt, seed=Lk)
+    q = torch.zeros(1, 2, 70, 64, dtype=DT[dt])
+    o, lse = gpu_forward(q, k, v, False, 0.125)
+    np.testing.assert_allclose(lse.double().numpy(), math.log(Lk), atol=TOL_LSE)
+    mean = to64(v).mean(axis=2, keepdims=True)
+    np.testing.assert_allclose(to64(o), np.broadcast_to(mean, o.shape),
+                               atol=TOL_O[dt])
+    # causal: LSE_i = ln(i + 1)
+    o, lse = gpu_forward(q, k, v, True, 0.125)
+    want = np.log(np.arange(1, 71, dtype=np.float64))
+    np.testing.assert_allclose(lse.double().numpy(),
+                               np.broadcast_to(want, lse.shape), atol=TOL_LSE)
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f16", 64), ("f32", 128)])
+def test_causal_row0_is_v0_exactly(dt, D):
+    say(f"[closed] causal row 0 {dt} D={D}")
+    q, k, v = inputs.make_qkv(2, 3, 200, 200, D, dt, seed=5)
+    o, lse = gpu_forward(q, k, v, True, 1.0 / math.sqrt(D))
+    assert torch.equal(o[:, :, 0, :], v[:, :, 0, :])
+    s00 = (to64(q)[:, :, 0] * to64(k)[:, :, 0]).sum(-1) / math.sqrt(D)
+    np.testing.assert_allclose(lse[:, :, 0].double().numpy(), s00, atol=TOL_LSE)
+
+
+def test_constant_v_rows():
+    say("[closed] constant V")
+    q, k, _ = inputs.make_qkv(1, 2, 300, 300, 128, "bf16", seed=6)
+    row = torch.randn(1, 2, 1, 128).to(torch.bfloat16)
+    v = row.expand(1, 2, 300, 128).contiguous()
+    for causal in (False, True):
+        o, _ = gpu_forward(q, k, v, causal, 0.088)
+        np.testing.assert_allclose(to64(o), np.broadcast_to(to64(row), o.shape),
+                                   atol=TOL_O["bf16"])
+
+
+# ------------------------------------------------ memory safety, determinism
+
+def test_no_writes_outside_outputs():
+    """Canary bands around O and LSE stay untouched (ragged Lq tail)."""
+    say("[safety] canaries")
+    B, H, Lq, Lk, D = 1, 2, 197, 301, 128
+    q, k, v = (t.cuda() for t in inputs.make_qkv(B, H, Lq, Lk, D, "bf16", 8))
+    pad = 4096
+    n_o = B * H * Lq * D
+    o_buf = torch.full((n_o + 2 * pad,), float("nan"), dtype=torch.bfloat16,
+                       device="cuda")
+    l_buf = torch.full((B * H * Lq + 2 * pad,), -7.0, dtype=torch.float32,
+                       device="cuda")
+    o = o_buf[pad:pad + n_o].view(B, H, Lq, D)
+    lse = l_buf[pad:pad + B * H * Lq].view(B, H, Lq)
+    for causal in (False, True):
+        fa.forward(q, k, v, causal=causal, scale=0.09, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.isnan(o_buf[:pad]).all() and torch.isnan(o_buf[-pad:]).all()
+        assert (l_buf[:pad] == -7.0).all() and (l_buf[-pad:] == -7.0).all()
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_bitwise_deterministic():
+    say("[safety] determinism")
+    q, k, v = (t.cuda() for t in inputs.make_qkv(2, 4, 1000, 1000, 128, "bf16", 9))
+    outs = []
+    for _ in range(3):
+        o, lse = fa.forward(q, k, v, causal=True)
+        torch.cuda.synchronize()
+        outs.append((o.clone(), lse.clone()))
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+
+
+def test_side_stream_and_no_lse():
+    say("[api] side stream, lse=NULL")
+    q, k, v = inputs.make_qkv(1, 2, 256, 384, 64, "f16", 10)
+    dq, dk, dv = (t.cuda() for t in (q, k, v))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = fa.forward(dq, dk, dv, causal=False, want_lse=False)
+    s.synchronize()
+    assert lse is None
+    ro, _ = oracle.attention(to64(q), to64(k), to64(v), False, 0.125)
+    assert np.abs(to64(o.cpu()) - ro).max() <= TOL_O["f16"]
+
+
+def test_host_pointer_is_rejected():
+    say("[api] host pointer")
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    d = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(d)
+    rc = fa.fa_fwd(q.data_ptr(), d.data_ptr(), d.data_ptr(), o.data_ptr(), None,
+                   1, 1, 64, 64, 64, 0, 0.125, 2, None)
+    assert rc == 8
+
+
+def test_native_library_is_the_one_loaded():
+    """The HIP library in the package is what runs (no fallback exists)."""
+    lib = fa.load()
+    maps = open("/proc/self/maps").read()
+    assert os.path.realpath(fa._lib.LIB_PATH) in maps
+    hip = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(hip) == 1, hip   # one HIP runtime shared with torch
+    assert lib is not None
