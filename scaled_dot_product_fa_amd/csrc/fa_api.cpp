@@ -75,8 +75,8 @@ fa::FwdArgs make_args(const void *q, const void *k, const void *v, void *o, floa
     return a;
 }
 
-// Tuning override "NWxQBxBN" (for sweeps), or "valu" to force the vector-ALU
-// kernel.  Unset means the built-in choice.
+// Tuning override "NWxQBxBNxOCCxPIPE" (for sweeps), or "valu" to force the
+// vector-ALU kernel.  Unset means the built-in choice.
 bool env_tile(fa::MfmaTile &t, bool &force_valu)
 {
     force_valu = false;
@@ -86,12 +86,13 @@ bool env_tile(fa::MfmaTile &t, bool &force_valu)
         force_valu = true;
         return false;
     }
-    int nw = 0, qb = 0, bn = 0;
-    char x1 = 0, x2 = 0;
+    int nw = 0, qb = 0, bn = 0, occ = 0, pipe = 0;
+    char x1 = 0, x2 = 0, x3 = 0, x4 = 0;
     char tail = 0;
-    const int n = sscanf(s, "%d%c%d%c%d%c", &nw, &x1, &qb, &x2, &bn, &tail);
-    if (n != 5 || x1 != 'x' || x2 != 'x') return false;
-    t = fa::MfmaTile{nw, qb, bn};
+    const int n = sscanf(s, "%d%c%d%c%d%c%d%c%d%c", &nw, &x1, &qb, &x2, &bn, &x3, &occ, &x4,
+                         &pipe, &tail);
+    if (n != 9 || x1 != 'x' || x2 != 'x' || x3 != 'x' || x4 != 'x') return false;
+    t = fa::MfmaTile{nw, qb, bn, occ, pipe};
     return true;
 }
 

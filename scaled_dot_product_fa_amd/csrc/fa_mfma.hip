@@ -139,8 +139,9 @@ __device__ __forceinline__ void decompose(int wg, int nwg, int BH, int ntq,
     if (causal) qt = ntq - 1 - qt;
 }
 
-template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN>
-__global__ __launch_bounds__(NW * 64) void fa_fwd_mfma_kernel(Params p)
+template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN, int OCC>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void fa_fwd_mfma_kernel(Params p)
 {
     constexpr int NT = NW * 64;          // threads
     constexpr int BM = NW * QB * 32;     // query rows per workgroup
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_mfma_kernel(Params p)
     constexpr int K_PER_T = BN * KCH / NT;       // K chunks loaded per thread
     constexpr int V_KEYS = BN * (D / 8) / NT;    // keys per thread in the V load
     static_assert(K_PER_T >= 1 && BN * KCH % NT == 0, "K tile split");
-    static_assert(V_KEYS == 2 || V_KEYS == 4 || V_KEYS == 8, "V tile split");
+    static_assert(V_KEYS == 1 || V_KEYS == 2 || V_KEYS == 4 || V_KEYS == 8, "V tile split");
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
@@ -256,7 +257,12 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_mfma_kernel(Params p)
             const int d = v_dc * 8 + e;
             const int pc = ch ^ (((d >> 3) ^ d) & (VCH - 1));
             uint8_t *dst = vb + d * VROW + pc * 16 + off;
-            uint32_t w[V_KEYS / 2];
+            if constexpr (V_KEYS == 1) {
+                const uint32_t a = vst[0][e >> 1];
+                *reinterpret_cast<uint16_t *>(dst) = (uint16_t)((e & 1) ? (a >> 16) : a);
+                continue;
+            }
+            uint32_t w[V_KEYS / 2 > 0 ? V_KEYS / 2 : 1];
 #pragma unroll
             for (int r = 0; r < V_KEYS / 2; ++r) {
                 const uint32_t a = vst[2 * r][e >> 1];
@@ -423,7 +429,461 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_mfma_kernel(Params p)
     }
 }
 
-template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN>
+// ---------------------------------------------------------------------------
+// Direct-load variant.  K and V tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at the wave's
+// LDS base + 16*i), so no VGPRs hold staged data and no LDS stores are
+// issued.  Both tiles stay row-major (key rows of D elements) with 16-byte
+// chunks XOR-swizzled by row; the swizzle is applied by choosing which global
+// chunk each lane fetches.  The V^T operand of the PV product is read with
+// ds_read_b64_tr_b16, which transposes 16-bit data inside each 16-lane group:
+// lane t receives element t%4 of the 8-byte blocks addressed by lanes
+// 4r + t/4 (r = 0..3).  So the lanes of a group address a 4-key x 16-dim
+// block and each lane gets 4 consecutive keys of one dim.  Two such reads
+// give the 8 keys of one lane's A operand.
+// ---------------------------------------------------------------------------
+
+// LDS swizzles for 64 banks of 4 bytes (256 bytes per bank cycle).
+//
+// K: a 16-byte read phase serves 16 lanes, which fetch rows
+// swap_bits23(0..15) of a 32-row block at one logical chunk.  D = 128 rows
+// are 256 bytes (every row starts on bank 0): XOR with the same permutation
+// gives the 16 lanes 16 distinct chunks.  D = 64 rows are 128 bytes (row
+// parity picks the bank half): XOR with the permutation shifted down by one
+// gives each parity class 8 distinct chunks.
+template <int D>
+__device__ __forceinline__ int swz_k(int row)
+{
+    if constexpr (D == 128) return swap_bits23(row & 15);
+    return (swap_bits23(row & 15) >> 1) & 7;
+}
+
+// V: an 8-byte transposed read phase serves 32 lanes, which touch 4
+// consecutive rows x 4 adjacent chunks (16 x 16 bytes).  D = 128: XOR the
+// chunk with 4*(row % 4) so each row lands on its own 64-byte bank quarter.
+// D = 64: rows r and r+2 share a bank half, so XOR with 4*((row/2) % 2).
+template <int D>
+__device__ __forceinline__ int swz_v(int row)
+{
+    if constexpr (D == 128) return 4 * (row & 3);
+    return 4 * ((row >> 1) & 1);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ uint2 ds_read_tr(const uint8_t *p)
+{
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
+template <typename Ops, int D, bool CAUSAL, int NW, int BN, int OCC, bool SWP>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void fa_fwd_mfma_dma_kernel(Params p)
+{
+    constexpr int NT = NW * 64;
+    constexpr int BM = NW * 32;          // one 32-query block per wave
+    constexpr int DC = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int KB = BN / 32;
+    constexpr int KC = BN / 16;
+    constexpr int ROWB = D * 2;          // bytes per K or V row in LDS
+    constexpr int KCH = D / 8;           // 16-byte chunks per row
+    constexpr int TILEB = BN * ROWB;     // bytes of one K (or V) tile
+    constexpr int LOADS = TILEB / (NT * 16);
+    static_assert(LOADS >= 1 && TILEB % (NT * 16) == 0, "tile split");
+    static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+
+    // Two buffers as distinct objects, so the compiler can tell the DMA into
+    // one buffer from the reads of the other.
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILEB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    int bh, qt;
+    decompose(blockIdx.x, gridDim.x, p.BH, p.ntq, CAUSAL, bh, qt);
+    const int q_first = qt * BM;
+    const int qw = q_first + wave * 32;
+
+    const uint16_t *qh = p.q + (int64_t)bh * p.Lq * D;
+    const uint16_t *kh = p.k + (int64_t)bh * p.Lk * D;
+    const uint16_t *vh = p.v + (int64_t)bh * p.Lk * D;
+
+    // ---- Q^T operand in VGPRs (rows past Lq read the last row; not stored)
+    u32x4 qreg[DC];
+    {
+        const int row = min(qw + l32, p.Lq - 1);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+            qreg[dc] = *reinterpret_cast<const u32x4 *>(qh + (uint32_t)row * D + dc * 16 + hi * 8);
+    }
+
+    // ---- per-lane DMA source offsets (bytes within a tile) and LDS slots
+    int ld_row[LOADS];
+    uint32_t ld_k[LOADS], ld_v[LOADS];
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+        const int slot = (r * NW + wave) * 64 + lane;
+        const int row = slot / KCH, pc = slot % KCH;
+        ld_row[r] = row;
+        ld_k[r] = (uint32_t)(row * D + (pc ^ swz_k<D>(row)) * 8) * 2;
+        ld_v[r] = (uint32_t)(row * D + (pc ^ swz_v<D>(row)) * 8) * 2;
+    }
+    auto issue_one = [&](const uint16_t *src, const uint32_t *offs, int k0, uint8_t *dst) {
+        const uint8_t *t = reinterpret_cast<const uint8_t *>(src + (int64_t)k0 * D);
+        const int last = p.Lk - 1 - k0;  // last valid row of this tile
+#pragma unroll
+        for (int r = 0; r < LOADS; ++r) {
+            uint32_t o = offs[r];
+            if (k0 + BN > p.Lk && ld_row[r] > last) {
+                // past the end of the keys: fetch any valid row (its scores
+                // are masked and its V rows get probability 0)
+                o -= (uint32_t)(ld_row[r] - last) * ROWB;
+            }
+            __builtin_amdgcn_global_load_lds(t + o, dst + (r * NW + wave) * 1024, 16, 0, 0);
+        }
+    };
+    auto issue_k = [&](int k0, uint8_t *kd) { issue_one(kh, ld_k, k0, kd); };
+    auto issue_v = [&](int k0, uint8_t *vd) { issue_one(vh, ld_v, k0, vd); };
+
+    // ---- per-lane LDS read offsets (loop invariant)
+    uint32_t k_rd[DC];
+    {
+        const int row = swap_bits23(l32);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+            k_rd[dc] = (uint32_t)(row * ROWB + (((dc * 2 + hi) ^ swz_k<D>(row)) * 16));
+    }
+    uint32_t v_rd[DB];
+    {
+        const int g = lane >> 4, t = lane & 15;
+        const int row = 8 * hi + (t >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + 16 * (g & 1) + 4 * (t & 3);   // element
+            const int c = col >> 3, within = (col & 7) * 2;
+            v_rd[db] = (uint32_t)(row * ROWB + ((c ^ swz_v<D>(row)) * 16) + within);
+        }
+    }
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float m_run = -INFINITY, l_part = 0.f;
+    const float c = p.c;
+
+    const int kv_end = CAUSAL ? min(p.Lk, q_first + BM) : p.Lk;
+    const int ntiles = (kv_end + BN - 1) / BN;
+    // wave-uniform: does this wave see any key of the tile starting at k0?
+    auto active = [&](int k0) { return qw < p.Lq && !(CAUSAL && k0 > qw + 31); };
+
+    struct STile {
+        f32x16 v[KB];
+    };
+    // S^T = K Q^T for one tile (raw scores, fp32)
+    auto qk = [&](const uint8_t *kb_) {
+        STile st;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st.v[kb][i] = 0.f;
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(kb_ + k_rd[dc] + kb * 32 * ROWB);
+                st.v[kb] = Ops::mma(a, qreg[dc], st.v[kb]);
+            }
+        }
+        return st;
+    };
+    // masking, online softmax and O^T += V^T P^T for one tile
+    auto softmax_pv = [&](STile st, int k0, const uint8_t *vb_) {
+        if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = k0 + kb * 32 + (i >> 3) * 16 + hi * 8 + (i & 7);
+                    const bool keep = key < p.Lk && (!CAUSAL || key <= qw + l32);
+                    st.v[kb][i] = keep ? st.v[kb][i] : -INFINITY;
+                }
+        }
+        // four independent partial maxima / sums keep the dependency
+        // chains short
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], st.v[kb][i]);
+        const float mx = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+        const float m_new = fmaxf(m_run, mx);
+        if (__any((m_new - m_run) * c > kLazyThreshold)) {
+            const float alpha = (m_new == -INFINITY) ? 1.f
+                                                     : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+            m_run = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        }
+        const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+        u32x4 pk[KC];
+        float r4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            float e[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                e[i] = __builtin_amdgcn_exp2f(fmaf(st.v[kb][i], c, -mc));
+                r4[i & 3] += e[i];
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                u32x4 x;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) x[w] = Ops::pack2(e[h * 8 + 2 * w], e[h * 8 + 2 * w + 1]);
+                pk[kb * 2 + h] = x;
+            }
+        }
+        l_part += (r4[0] + r4[1]) + (r4[2] + r4[3]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const uint8_t *vp = vb_ + v_rd[db] + kc * 16 * ROWB;
+                const uint2 lo = ds_read_tr(vp);
+                const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
+                const u32x4 a = {lo.x, lo.y, hi4.x, hi4.y};
+                oacc[db] = Ops::mma(a, pk[kc], oacc[db]);
+            }
+    };
+    auto sync_tiles = [&]() {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    if constexpr (!SWP) {
+        // one tile per step: K_j and V_j are loaded together, one step ahead
+        issue_k(0, k_lds0);
+        issue_v(0, v_lds0);
+        sync_tiles();
+        for (int j = 0; j < ntiles; j += 2) {
+            if (j + 1 < ntiles) {
+                issue_k((j + 1) * BN, k_lds1);
+                issue_v((j + 1) * BN, v_lds1);
+            }
+            if (active(j * BN)) softmax_pv(qk(k_lds0), j * BN, v_lds0);
+            sync_tiles();
+            if (j + 1 >= ntiles) break;
+            if (j + 2 < ntiles) {
+                issue_k((j + 2) * BN, k_lds0);
+                issue_v((j + 2) * BN, v_lds0);
+            }
+            if (active((j + 1) * BN)) softmax_pv(qk(k_lds1), (j + 1) * BN, v_lds1);
+            sync_tiles();
+        }
+    } else {
+        // Software pipeline: step j runs the QK^T MFMAs of tile j+1 while
+        // the vector ALUs run the softmax of tile j, then adds P_j V_j.  K
+        // therefore runs one tile ahead of V: during step j the DMA fills
+        // K_{j+2} and V_{j+1}, into the buffers that K_j and V_{j-1} left at
+        // the end of step j-1.  Each step is branch-free apart from the DMA
+        // guards and the mask at its start and the rare rescale, and
+        // sched_group_barrier pins the MFMA / LDS-read / VALU interleave of
+        // the two straight-line blocks.  Tiles past a wave's diagonal are not
+        // skipped: they are fully masked and contribute p = 0.
+        // MFMAs of the next tile's QK^T issued before / after the rescale
+        // branch, and VALU slots given to each MFMA of the second half
+        constexpr int HALF = KB * DC / 2;
+        constexpr int VALU_B = (3 * KB * 16 + KB * 8) / (KB * DC - HALF);
+        issue_k(0, k_lds0);
+        issue_v(0, v_lds0);
+        if (ntiles > 1) issue_k(BN, k_lds1);
+        sync_tiles();
+        STile cur;
+        cur = qk(k_lds0);  // (assigned, not initialised: keeps clang from
+                           // trying to constant-fold the call)
+        __syncthreads();   // everyone is done with K_0 before K_2 lands there
+
+        auto step = [&](int j, const uint8_t *k_next, const uint8_t *v_cur, uint8_t *k_dma,
+                        uint8_t *v_dma) {
+            if (j + 2 < ntiles) issue_k((j + 2) * BN, k_dma);
+            if (j + 1 < ntiles) issue_v((j + 1) * BN, v_dma);
+            const int k0 = j * BN;
+            if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = k0 + kb * 32 + (i >> 3) * 16 + hi * 8 + (i & 7);
+                        const bool keep = key < p.Lk && (!CAUSAL || key <= qw + l32);
+                        cur.v[kb][i] = keep ? cur.v[kb][i] : -INFINITY;
+                    }
+            }
+            // block A: row max of tile j | first half of QK^T for tile j+1
+            STile nxt;
+            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], cur.v[kb][i]);
+#pragma unroll
+            for (int n = 0; n < HALF; ++n) {
+                const int kb = n / DC, dc = n % DC;
+                if (dc == 0) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) nxt.v[kb][i] = 0.f;
+                }
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(k_next + k_rd[dc] + kb * 32 * ROWB);
+                nxt.v[kb] = Ops::mma(a, qreg[dc], nxt.v[kb]);
+            }
+            const float mx = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+            const float m_new = fmaxf(m_run, mx);
+            const bool grow = (m_new - m_run) * c > kLazyThreshold;
+            // LDS reads run three MFMAs ahead of their use
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);       // LDS read
+#pragma unroll
+            for (int n = 0; n < HALF; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+            }
+            if (__any(grow)) {
+                const float alpha = (m_new == -INFINITY)
+                                        ? 1.f
+                                        : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+                m_run = m_new;
+                l_part *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            }
+            // block B: exponentials of tile j | second half of QK^T for
+            // tile j+1, then O^T += V^T P^T for tile j
+            const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+            u32x4 pk[KC];
+            float e[KB][16];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    e[kb][i] = __builtin_amdgcn_exp2f(fmaf(cur.v[kb][i], c, -mc));
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    u32x4 x;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        x[w] = Ops::pack2(e[kb][h * 8 + 2 * w], e[kb][h * 8 + 2 * w + 1]);
+                    pk[kb * 2 + h] = x;
+                }
+#pragma unroll
+            for (int n = HALF; n < KB * DC; ++n) {
+                const int kb = n / DC, dc = n % DC;
+                if (dc == 0) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) nxt.v[kb][i] = 0.f;
+                }
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(k_next + k_rd[dc] + kb * 32 * ROWB);
+                nxt.v[kb] = Ops::mma(a, qreg[dc], nxt.v[kb]);
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    const uint8_t *vp = v_cur + v_rd[db] + kc * 16 * ROWB;
+                    const uint2 lo = ds_read_tr(vp);
+                    const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
+                    const u32x4 a = {lo.x, lo.y, hi4.x, hi4.y};
+                    oacc[db] = Ops::mma(a, pk[kc], oacc[db]);
+                }
+            float r4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) r4[i & 3] += e[kb][i];
+            l_part += (r4[0] + r4[1]) + (r4[2] + r4[3]);
+            // K reads three MFMAs ahead; the transposed V reads start during
+            // the exponentials and stay two PV MFMAs ahead
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);            // LDS read
+#pragma unroll
+            for (int n = HALF; n < KB * DC; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);        // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);        // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, VALU_B, 1);   // VALU
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);            // LDS read
+#pragma unroll
+            for (int n = 0; n < DB * KC; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);   // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);   // VALU
+            }
+            cur = nxt;
+            sync_tiles();
+        };
+        for (int j = 0; j < ntiles; j += 2) {
+            step(j, k_lds1, v_lds0, k_lds0, v_lds1);
+            if (j + 1 >= ntiles) break;
+            step(j + 1, k_lds0, v_lds1, k_lds1, v_lds0);
+        }
+    }
+
+    // ---- epilogue
+    const float l = half_sum(l_part);
+    const int row = qw + l32;
+    if (row < p.Lq) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t *orow = p.o + ((int64_t)bh * p.Lq + row) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = db * 32 + g * 8 + hi * 4;
+                u32x2 x = {Ops::pack2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                           Ops::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(orow + d) = x;
+            }
+        if (p.lse != nullptr && hi == 0)
+            p.lse[(int64_t)bh * p.Lq + row] = l > 0.f ? m_run * p.scale + __logf(l) : -INFINITY;
+    }
+}
+
+template <typename Ops, int D, bool CAUSAL, int NW, int BN, int OCC, bool SWP>
+hipError_t launch_dma(const FwdArgs &a)
+{
+    constexpr int BM = NW * 32;
+    Params p;
+    p.q = static_cast<const uint16_t *>(a.q);
+    p.k = static_cast<const uint16_t *>(a.k);
+    p.v = static_cast<const uint16_t *>(a.v);
+    p.o = static_cast<uint16_t *>(a.o);
+    p.lse = a.lse;
+    p.BH = (int)(a.B * a.H);
+    p.Lq = (int)a.Lq;
+    p.Lk = (int)a.Lk;
+    p.ntq = (int)((a.Lq + BM - 1) / BM);
+    p.scale = a.scale;
+    p.c = a.scale * kLog2e;
+    const int64_t nwg = (int64_t)p.BH * p.ntq;
+    hipLaunchKernelGGL((fa_fwd_mfma_dma_kernel<Ops, D, CAUSAL, NW, BN, OCC, SWP>),
+                       dim3((unsigned)nwg), dim3(NW * 64), 0, a.stream, p);
+    return hipGetLastError();
+}
+
+template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN, int OCC>
 hipError_t launch_cfg(const FwdArgs &a)
 {
     constexpr int BM = NW * QB * 32;
@@ -440,7 +900,7 @@ hipError_t launch_cfg(const FwdArgs &a)
     p.scale = a.scale;
     p.c = a.scale * kLog2e;
     const int64_t nwg = (int64_t)p.BH * p.ntq;
-    hipLaunchKernelGGL((fa_fwd_mfma_kernel<Ops, D, CAUSAL, NW, QB, BN>),
+    hipLaunchKernelGGL((fa_fwd_mfma_kernel<Ops, D, CAUSAL, NW, QB, BN, OCC>),
                        dim3((unsigned)nwg), dim3(NW * 64), 0, a.stream, p);
     return hipGetLastError();
 }
@@ -448,14 +908,46 @@ hipError_t launch_cfg(const FwdArgs &a)
 template <typename Ops, int D, bool CAUSAL>
 hipError_t launch_tile(const FwdArgs &a, const MfmaTile &t)
 {
-    if (t.nw == 4 && t.qb == 1 && t.bn == 64) return launch_cfg<Ops, D, CAUSAL, 4, 1, 64>(a);
-    if (t.nw == 4 && t.qb == 2 && t.bn == 64) return launch_cfg<Ops, D, CAUSAL, 4, 2, 64>(a);
+    if (t.nw == 4 && t.qb == 1 && t.bn == 64 && t.occ == 1)
+        return launch_cfg<Ops, D, CAUSAL, 4, 1, 64, 1>(a);
+    if (t.nw == 4 && t.qb == 1 && t.bn == 64 && t.occ == 2)
+        return launch_cfg<Ops, D, CAUSAL, 4, 1, 64, 2>(a);
+    if (t.nw == 8 && t.qb == 1 && t.bn == 64 && t.occ == 2)
+        return launch_cfg<Ops, D, CAUSAL, 8, 1, 64, 2>(a);
+    if (t.nw == 4 && t.qb == 2 && t.bn == 64 && t.occ == 1)
+        return launch_cfg<Ops, D, CAUSAL, 4, 2, 64, 1>(a);
+    return hipErrorInvalidConfiguration;
+}
+
+template <typename Ops, int D, bool CAUSAL>
+hipError_t launch_tile_dma(const FwdArgs &a, const MfmaTile &t)
+{
+    if (t.qb != 1) return hipErrorInvalidConfiguration;
+    const bool swp = t.pipe == 2;
+    if (t.nw == 8 && t.bn == 64 && t.occ == 2)
+        return swp ? launch_dma<Ops, D, CAUSAL, 8, 64, 2, true>(a)
+                   : launch_dma<Ops, D, CAUSAL, 8, 64, 2, false>(a);
+    if (t.nw == 4 && t.bn == 64 && t.occ == 2)
+        return swp ? launch_dma<Ops, D, CAUSAL, 4, 64, 2, true>(a)
+                   : launch_dma<Ops, D, CAUSAL, 4, 64, 2, false>(a);
+    if constexpr (D == 128) {
+        if (t.nw == 8 && t.bn == 32 && t.occ == 2)
+            return swp ? launch_dma<Ops, D, CAUSAL, 8, 32, 2, true>(a)
+                       : launch_dma<Ops, D, CAUSAL, 8, 32, 2, false>(a);
+    }
     return hipErrorInvalidConfiguration;
 }
 
 template <typename Ops>
 hipError_t launch_ops(const FwdArgs &a, const MfmaTile &t)
 {
+    if (t.pipe == 1 || t.pipe == 2) {
+        if (a.D == 64)
+            return a.causal ? launch_tile_dma<Ops, 64, true>(a, t)
+                            : launch_tile_dma<Ops, 64, false>(a, t);
+        return a.causal ? launch_tile_dma<Ops, 128, true>(a, t)
+                        : launch_tile_dma<Ops, 128, false>(a, t);
+    }
     if (a.D == 64)
         return a.causal ? launch_tile<Ops, 64, true>(a, t) : launch_tile<Ops, 64, false>(a, t);
     return a.causal ? launch_tile<Ops, 128, true>(a, t) : launch_tile<Ops, 128, false>(a, t);
@@ -470,8 +962,13 @@ bool mfma_supported(const FwdArgs &a)
 
 MfmaTile mfma_choose_tile(const FwdArgs &a)
 {
-    (void)a;
-    return MfmaTile{4, 1, 64};
+    // Direct loads with the software-pipelined step.  8 waves (256 query
+    // rows) per workgroup when that still gives at least two workgroups per
+    // CU (512 for 256 CUs); otherwise 4 waves (128 rows) for more
+    // workgroups.
+    const int64_t wgs256 = a.B * a.H * ((a.Lq + 255) / 256);
+    if (wgs256 >= 512) return MfmaTile{8, 1, 64, 2, 2};
+    return MfmaTile{4, 1, 64, 2, 2};
 }
 
 const char *mfma_kernel_name(const FwdArgs &a, const MfmaTile &t)
