@@ -105,7 +105,7 @@ def parity_rows(w, causal, r, n_random=8):
                 max_abs_lse=float(np.abs(gl - rl).max()))
 
 
-def cpu_baseline(w, causal, r, budget_s=12.0):
+def cpu_baseline(w, causal, r, budget_s=15.0):
     """The fp64 oracle on a bounded, seeded row sample of the same workload,
     throughput scaled to TFLOP/s by the same FLOP formula (per row:
     4*Lk_visible*D)."""
@@ -126,8 +126,9 @@ def cpu_baseline(w, causal, r, budget_s=12.0):
         oracle.attention_rows(q, k, v, ids, causal, w.scale)
         return fl, time.perf_counter() - t0
 
-    fl, dt = run(64)
-    n = int(min(total_rows, max(64, 64 * budget_s / max(dt, 1e-3))))
+    pilot = 2048
+    fl, dt = run(pilot)
+    n = int(min(total_rows, max(pilot, pilot * budget_s / max(dt, 1e-3))))
     fl, dt = run(n)
     return dict(value=fl / dt / 1e12, unit="TFLOP/s",
                 cores=oracle.num_threads(), kind="oracle",
@@ -152,8 +153,8 @@ def traffic(kernel_name, launches_per_measure=1):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="mid")
     ap.add_argument("--causal", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

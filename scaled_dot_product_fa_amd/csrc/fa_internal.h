@@ -24,7 +24,8 @@ struct FwdArgs {
 // BN keys per K/V tile, OCC waves per SIMD the register budget is cut for,
 // and the K/V staging pipe (0: through VGPRs with a transposing V store,
 // 1: direct global-to-LDS loads with transposed V reads, 2: as 1 with the
-// QK^T of the next tile software-pipelined under the softmax of this one).
+// QK^T of the next tile software-pipelined under the softmax of this one,
+// 3: as 2 with the loads issued one more tile ahead into triple buffers).
 struct MfmaTile {
     int nw, qb, bn, occ, pipe;
 };

@@ -478,7 +478,13 @@ __device__ __forceinline__ uint2 ds_read_tr(const uint8_t *p)
     return __builtin_bit_cast(uint2, r);
 }
 
-template <typename Ops, int D, bool CAUSAL, int NW, int BN, int OCC, bool SWP>
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <typename Ops, int D, bool CAUSAL, int NW, int BN, int OCC, bool SWP, int STAGES>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_fwd_mfma_dma_kernel(Params p)
 {
@@ -501,10 +507,15 @@ void fa_fwd_mfma_dma_kernel(Params p)
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILEB];
+    // third buffers only for the three-stage pipeline
+    constexpr int TILEB3 = STAGES == 3 ? TILEB : 16;
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds2[TILEB3];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds2[TILEB3];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave index as a scalar, so LDS DMA destinations stay in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
@@ -539,11 +550,17 @@ void fa_fwd_mfma_dma_kernel(Params p)
     }
     auto issue_one = [&](const uint16_t *src, const uint32_t *offs, int k0, uint8_t *dst) {
         const uint8_t *t = reinterpret_cast<const uint8_t *>(src + (int64_t)k0 * D);
+        if (k0 + BN <= p.Lk) {   // uniform: every row of the tile exists
+#pragma unroll
+            for (int r = 0; r < LOADS; ++r)
+                __builtin_amdgcn_global_load_lds(t + offs[r], dst + (r * NW + wave) * 1024, 16, 0, 0);
+            return;
+        }
         const int last = p.Lk - 1 - k0;  // last valid row of this tile
 #pragma unroll
         for (int r = 0; r < LOADS; ++r) {
             uint32_t o = offs[r];
-            if (k0 + BN > p.Lk && ld_row[r] > last) {
+            if (ld_row[r] > last) {
                 // past the end of the keys: fetch any valid row (its scores
                 // are masked and its V rows get probability 0)
                 o -= (uint32_t)(ld_row[r] - last) * ROWB;
@@ -705,20 +722,33 @@ void fa_fwd_mfma_dma_kernel(Params p)
         // MFMAs of the next tile's QK^T issued before / after the rescale
         // branch, and VALU slots given to each MFMA of the second half
         constexpr int HALF = KB * DC / 2;
-        constexpr int VALU_B = (3 * KB * 16 + KB * 8) / (KB * DC - HALF);
+        // per 8-key chunk of P: 8 FMA + 8 exp + 8 add + 4 convert
+        constexpr int VALU_P = 28;
+        constexpr int VALU_B = 2 * VALU_P / (KB * DC - HALF);
+        constexpr int VALU_C = (KC > 2 ? (KC - 2) * VALU_P : 0) / (DB * KC) + 1;
+        // With STAGES = 3 the DMA runs one more step ahead: step j fills
+        // K_{j+3} and V_{j+2}, and its closing wait covers only the loads of
+        // the step before (vmcnt counts the newer ones still in flight).
+        constexpr int AHEAD = STAGES - 1;
         issue_k(0, k_lds0);
         issue_v(0, v_lds0);
         if (ntiles > 1) issue_k(BN, k_lds1);
         sync_tiles();
+        if constexpr (STAGES == 3) {
+            if (ntiles > 2) issue_k(2 * BN, k_lds2);
+            if (ntiles > 1) issue_v(BN, v_lds1);
+        }
         STile cur;
         cur = qk(k_lds0);  // (assigned, not initialised: keeps clang from
                            // trying to constant-fold the call)
-        __syncthreads();   // everyone is done with K_0 before K_2 lands there
+        __syncthreads();   // everyone is done with K_0 before the DMA refills it
 
         auto step = [&](int j, const uint8_t *k_next, const uint8_t *v_cur, uint8_t *k_dma,
                         uint8_t *v_dma) {
-            if (j + 2 < ntiles) issue_k((j + 2) * BN, k_dma);
-            if (j + 1 < ntiles) issue_v((j + 1) * BN, v_dma);
+            const bool dma_k = j + AHEAD + 1 < ntiles;
+            const bool dma_v = j + AHEAD < ntiles;
+            if (dma_k) issue_k((j + AHEAD + 1) * BN, k_dma);
+            if (dma_v) issue_v((j + AHEAD) * BN, v_dma);
             const int k0 = j * BN;
             if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
 #pragma unroll
@@ -769,26 +799,29 @@ void fa_fwd_mfma_dma_kernel(Params p)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
             }
-            // block B: exponentials of tile j | second half of QK^T for
-            // tile j+1, then O^T += V^T P^T for tile j
+            // block B: second half of QK^T for tile j+1 under the
+            // exponentials of key chunks 0-1 of tile j; then O^T += V^T P^T
+            // chunk by chunk, with the exponentials of chunks 2-3 under the
+            // PV MFMAs of chunks 0-1.  That keeps MFMA and VALU work
+            // balanced inside each phase.
             const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-            u32x4 pk[KC];
-            float e[KB][16];
+            float r4[4] = {0.f, 0.f, 0.f, 0.f};
+            auto make_p = [&](int kc) {
+                const int kb = kc >> 1, h = kc & 1;
+                float e[8];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    e[kb][i] = __builtin_amdgcn_exp2f(fmaf(cur.v[kb][i], c, -mc));
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    u32x4 x;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        x[w] = Ops::pack2(e[kb][h * 8 + 2 * w], e[kb][h * 8 + 2 * w + 1]);
-                    pk[kb * 2 + h] = x;
+                for (int i = 0; i < 8; ++i) {
+                    e[i] = __builtin_amdgcn_exp2f(fmaf(cur.v[kb][h * 8 + i], c, -mc));
+                    r4[i & 3] += e[i];
                 }
+                u32x4 x;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) x[w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
+                return x;
+            };
+            u32x4 pk[KC];
+            pk[0] = make_p(0);
+            pk[1] = make_p(1);
 #pragma unroll
             for (int n = HALF; n < KB * DC; ++n) {
                 const int kb = n / DC, dc = n % DC;
@@ -800,23 +833,20 @@ void fa_fwd_mfma_dma_kernel(Params p)
                 nxt.v[kb] = Ops::mma(a, qreg[dc], nxt.v[kb]);
             }
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+            for (int kc = 0; kc < KC; ++kc) {
+                if (kc + 2 < KC) pk[kc + 2] = make_p(kc + 2);
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
+                for (int db = 0; db < DB; ++db) {
                     const uint8_t *vp = v_cur + v_rd[db] + kc * 16 * ROWB;
                     const uint2 lo = ds_read_tr(vp);
                     const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
                     const u32x4 a = {lo.x, lo.y, hi4.x, hi4.y};
                     oacc[db] = Ops::mma(a, pk[kc], oacc[db]);
                 }
-            float r4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) r4[i & 3] += e[kb][i];
+            }
             l_part += (r4[0] + r4[1]) + (r4[2] + r4[3]);
-            // K reads three MFMAs ahead; the transposed V reads start during
-            // the exponentials and stay two PV MFMAs ahead
+            // K reads three MFMAs ahead; the transposed V reads stay two PV
+            // MFMAs ahead
             __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);            // LDS read
 #pragma unroll
             for (int n = HALF; n < KB * DC; ++n) {
@@ -827,17 +857,35 @@ void fa_fwd_mfma_dma_kernel(Params p)
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);            // LDS read
 #pragma unroll
             for (int n = 0; n < DB * KC; ++n) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);   // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);   // VALU
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);        // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);        // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, VALU_C, 1);   // VALU
             }
             cur = nxt;
-            sync_tiles();
+            if constexpr (STAGES == 3) {
+                // wait for the previous step's loads only
+                if (dma_k && dma_v) wait_vmcnt<2 * LOADS>();
+                else if (dma_k || dma_v) wait_vmcnt<LOADS>();
+                else wait_vmcnt<0>();
+                __syncthreads();
+            } else {
+                sync_tiles();
+            }
         };
-        for (int j = 0; j < ntiles; j += 2) {
-            step(j, k_lds1, v_lds0, k_lds0, v_lds1);
-            if (j + 1 >= ntiles) break;
-            step(j + 1, k_lds0, v_lds1, k_lds1, v_lds0);
+        if constexpr (STAGES == 3) {
+            for (int j = 0; j < ntiles; j += 3) {
+                step(j, k_lds1, v_lds0, k_lds0, v_lds2);
+                if (j + 1 >= ntiles) break;
+                step(j + 1, k_lds2, v_lds1, k_lds1, v_lds0);
+                if (j + 2 >= ntiles) break;
+                step(j + 2, k_lds0, v_lds2, k_lds2, v_lds1);
+            }
+        } else {
+            for (int j = 0; j < ntiles; j += 2) {
+                step(j, k_lds1, v_lds0, k_lds0, v_lds1);
+                if (j + 1 >= ntiles) break;
+                step(j + 1, k_lds0, v_lds1, k_lds1, v_lds0);
+            }
         }
     }
 
@@ -861,7 +909,7 @@ void fa_fwd_mfma_dma_kernel(Params p)
     }
 }
 
-template <typename Ops, int D, bool CAUSAL, int NW, int BN, int OCC, bool SWP>
+template <typename Ops, int D, bool CAUSAL, int NW, int BN, int OCC, bool SWP, int STAGES>
 hipError_t launch_dma(const FwdArgs &a)
 {
     constexpr int BM = NW * 32;
@@ -878,7 +926,7 @@ hipError_t launch_dma(const FwdArgs &a)
     p.scale = a.scale;
     p.c = a.scale * kLog2e;
     const int64_t nwg = (int64_t)p.BH * p.ntq;
-    hipLaunchKernelGGL((fa_fwd_mfma_dma_kernel<Ops, D, CAUSAL, NW, BN, OCC, SWP>),
+    hipLaunchKernelGGL((fa_fwd_mfma_dma_kernel<Ops, D, CAUSAL, NW, BN, OCC, SWP, STAGES>),
                        dim3((unsigned)nwg), dim3(NW * 64), 0, a.stream, p);
     return hipGetLastError();
 }
@@ -919,29 +967,27 @@ hipError_t launch_tile(const FwdArgs &a, const MfmaTile &t)
     return hipErrorInvalidConfiguration;
 }
 
+template <typename Ops, int D, bool CAUSAL, int NW, int BN, int OCC>
+hipError_t launch_pipe(const FwdArgs &a, int pipe)
+{
+    if (pipe == 1) return launch_dma<Ops, D, CAUSAL, NW, BN, OCC, false, 2>(a);
+    if (pipe == 2) return launch_dma<Ops, D, CAUSAL, NW, BN, OCC, true, 2>(a);
+    return launch_dma<Ops, D, CAUSAL, NW, BN, OCC, true, 3>(a);
+}
+
 template <typename Ops, int D, bool CAUSAL>
 hipError_t launch_tile_dma(const FwdArgs &a, const MfmaTile &t)
 {
     if (t.qb != 1) return hipErrorInvalidConfiguration;
-    const bool swp = t.pipe == 2;
-    if (t.nw == 8 && t.bn == 64 && t.occ == 2)
-        return swp ? launch_dma<Ops, D, CAUSAL, 8, 64, 2, true>(a)
-                   : launch_dma<Ops, D, CAUSAL, 8, 64, 2, false>(a);
-    if (t.nw == 4 && t.bn == 64 && t.occ == 2)
-        return swp ? launch_dma<Ops, D, CAUSAL, 4, 64, 2, true>(a)
-                   : launch_dma<Ops, D, CAUSAL, 4, 64, 2, false>(a);
-    if constexpr (D == 128) {
-        if (t.nw == 8 && t.bn == 32 && t.occ == 2)
-            return swp ? launch_dma<Ops, D, CAUSAL, 8, 32, 2, true>(a)
-                       : launch_dma<Ops, D, CAUSAL, 8, 32, 2, false>(a);
-    }
+    if (t.nw == 8 && t.bn == 64 && t.occ == 2) return launch_pipe<Ops, D, CAUSAL, 8, 64, 2>(a, t.pipe);
+    if (t.nw == 4 && t.bn == 64 && t.occ == 2) return launch_pipe<Ops, D, CAUSAL, 4, 64, 2>(a, t.pipe);
     return hipErrorInvalidConfiguration;
 }
 
 template <typename Ops>
 hipError_t launch_ops(const FwdArgs &a, const MfmaTile &t)
 {
-    if (t.pipe == 1 || t.pipe == 2) {
+    if (t.pipe >= 1 && t.pipe <= 3) {
         if (a.D == 64)
             return a.causal ? launch_tile_dma<Ops, 64, true>(a, t)
                             : launch_tile_dma<Ops, 64, false>(a, t);
