@@ -14,8 +14,8 @@ published 2.5 PFLOP/s dense bf16 peak, and HBM traffic from the committed
 rocprofv3 counter summary when it matches the current kernel source),
 ``cpu_baseline`` (the fp64 CPU oracle timed on a bounded row sample of the
 same workload), ``parity`` (sampled rows of this run's output against the
-oracle) and ``secondary`` (the 16K non-causal forward, the other shape the
-metric names).
+oracle) and, with --secondary, ``secondary`` (the 16K non-causal forward,
+the other shape the metric names).
 """
 from __future__ import annotations
 
@@ -137,14 +137,16 @@ def cpu_baseline(w, causal, r, budget_s=15.0):
                 seconds=dt)
 
 
-def traffic(kernel_name, launches_per_measure=1):
-    """HBM bytes per launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+def traffic(kernel_name, workload):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by what the
+    counter reads for a plain copy of known size) from the committed
+    rocprofv3 summary for this kernel and workload, if it was taken on the
+    current kernel source; else None."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    rec = t.get(kernel_name)
+    rec = t.get(f"{kernel_name} {workload}")
     if not rec or rec.get("source_sha") != kernel_source_sha():
         return None
     return rec.get("bytes_per_launch")
@@ -158,7 +160,12 @@ def main():
     ap.add_argument("--workload", default="mid")
     ap.add_argument("--causal", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary", action="store_true",
+                    help="also time the 16K non-causal forward (the other "
+                         "shape the metric names); off by default so that a "
+                         "profile of the default command sees one workload")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help=argparse.SUPPRESS)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for scaling "
                          "HBM byte counters), then exit")
@@ -219,7 +226,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic(r["kernel"]),
+            "traffic": traffic(r["kernel"], workload_desc(w, causal)),
             "kernel": r["kernel"],
             "flops_per_launch": r["flops"],
             "kernel_ms": round(r["kernel_ms"], 5),
@@ -228,7 +235,7 @@ def main():
     log("bench: parity rows vs oracle ...")
     out["parity"] = parity_rows(w, causal, r)
     log(f"bench: parity {out['parity']}")
-    if not args.no_secondary and args.workload == "mid":
+    if args.secondary and args.workload == "mid":
         w2 = inputs.CONFIGS["long"]
         r2 = time_forward(w2, False, max(5, args.steps // 8),
                           max(2, args.warmup // 2))
