@@ -22,10 +22,10 @@ struct FwdArgs {
 // Tile shape of the MFMA kernel: NW waves per workgroup, each wave owning
 // QB blocks of 32 queries (so BM = NW * QB * 32 query rows per workgroup),
 // BN keys per K/V tile, OCC waves per SIMD the register budget is cut for,
-// and the K/V staging pipe (0: through VGPRs with a transposing V store,
-// 1: direct global-to-LDS loads with transposed V reads, 2: as 1 with the
-// QK^T of the next tile software-pipelined under the softmax of this one,
-// 3: as 2 with the loads issued one more tile ahead into triple buffers).
+// and the K/V staging pipe (0: through VGPRs with a transposing V store and
+// one tile per step; 2: direct global-to-LDS loads, transposed V reads, and
+// the QK^T of the next tile software-pipelined under the softmax of this
+// one).
 struct MfmaTile {
     int nw, qb, bn, occ, pipe;
 };

@@ -484,33 +484,31 @@ __device__ __forceinline__ void wait_vmcnt()
     __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <typename Ops, int D, bool CAUSAL, int NW, int BN, int OCC, bool SWP, int STAGES>
+template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN, int OCC>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_fwd_mfma_dma_kernel(Params p)
 {
     constexpr int NT = NW * 64;
-    constexpr int BM = NW * 32;          // one 32-query block per wave
-    constexpr int DC = D / 16;
-    constexpr int DB = D / 32;
-    constexpr int KB = BN / 32;
-    constexpr int KC = BN / 16;
+    constexpr int BM = NW * QB * 32;     // query rows per workgroup
+    constexpr int DC = D / 16;           // 16-dim chunks (k of the QK^T MFMA)
+    constexpr int DB = D / 32;           // 32-dim blocks (rows of O^T)
+    constexpr int KB = BN / 32;          // 32-key blocks (rows of S^T)
+    constexpr int KC = BN / 16;          // 16-key chunks (k of the PV MFMA)
     constexpr int ROWB = D * 2;          // bytes per K or V row in LDS
     constexpr int KCH = D / 8;           // 16-byte chunks per row
     constexpr int TILEB = BN * ROWB;     // bytes of one K (or V) tile
     constexpr int LOADS = TILEB / (NT * 16);
+    constexpr int NQK = KB * DC;         // K reads (A operands) per QK^T
+    constexpr int HALF = NQK / 2;        // ... issued before the rescale branch
     static_assert(LOADS >= 1 && TILEB % (NT * 16) == 0, "tile split");
-    static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+    static_assert(BN % 32 == 0 && D % 32 == 0 && KC >= 2, "tile shape");
 
-    // Two buffers as distinct objects, so the compiler can tell the DMA into
-    // one buffer from the reads of the other.
+    // Two buffers per operand as distinct objects, so the compiler can tell
+    // the DMA into one buffer from the reads of the other.
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILEB];
-    // third buffers only for the three-stage pipeline
-    constexpr int TILEB3 = STAGES == 3 ? TILEB : 16;
-    __shared__ __attribute__((aligned(1024))) uint8_t k_lds2[TILEB3];
-    __shared__ __attribute__((aligned(1024))) uint8_t v_lds2[TILEB3];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -522,19 +520,20 @@ void fa_fwd_mfma_dma_kernel(Params p)
     int bh, qt;
     decompose(blockIdx.x, gridDim.x, p.BH, p.ntq, CAUSAL, bh, qt);
     const int q_first = qt * BM;
-    const int qw = q_first + wave * 32;
+    const int qw = q_first + wave * QB * 32;   // first query row of this wave
 
     const uint16_t *qh = p.q + (int64_t)bh * p.Lq * D;
     const uint16_t *kh = p.k + (int64_t)bh * p.Lk * D;
     const uint16_t *vh = p.v + (int64_t)bh * p.Lk * D;
 
     // ---- Q^T operand in VGPRs (rows past Lq read the last row; not stored)
-    u32x4 qreg[DC];
-    {
-        const int row = min(qw + l32, p.Lq - 1);
+    u32x4 qreg[QB][DC];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const int row = min(qw + b * 32 + l32, p.Lq - 1);
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
-            qreg[dc] = *reinterpret_cast<const u32x4 *>(qh + (uint32_t)row * D + dc * 16 + hi * 8);
+            qreg[b][dc] = *reinterpret_cast<const u32x4 *>(qh + (uint32_t)row * D + dc * 16 + hi * 8);
     }
 
     // ---- per-lane DMA source offsets (bytes within a tile) and LDS slots
@@ -591,328 +590,237 @@ void fa_fwd_mfma_dma_kernel(Params p)
         }
     }
 
-    f32x16 oacc[DB];
+    f32x16 oacc[DB][QB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    float m_run = -INFINITY, l_part = 0.f;
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][b][i] = 0.f;
+    float m_run[QB], l_part[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        m_run[b] = -INFINITY;
+        l_part[b] = 0.f;
+    }
     const float c = p.c;
 
     const int kv_end = CAUSAL ? min(p.Lk, q_first + BM) : p.Lk;
     const int ntiles = (kv_end + BN - 1) / BN;
-    // wave-uniform: does this wave see any key of the tile starting at k0?
-    auto active = [&](int k0) { return qw < p.Lq && !(CAUSAL && k0 > qw + 31); };
 
     struct STile {
-        f32x16 v[KB];
+        f32x16 v[KB][QB];
     };
-    // S^T = K Q^T for one tile (raw scores, fp32)
-    auto qk = [&](const uint8_t *kb_) {
-        STile st;
+    // MFMAs n in [n0, n1) of S^T = K Q^T for one tile, ordered dc-major so
+    // the KB*QB accumulators form independent chains; each K read (A
+    // operand) feeds QB MFMAs.
+    auto qk_part = [&](STile &st, const uint8_t *kbuf, int n0, int n1) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int n = n0; n < n1; ++n) {
+            const int dc = n / KB, kb = n % KB;
+            if (dc == 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) st.v[kb][i] = 0.f;
+                for (int b = 0; b < QB; ++b)
 #pragma unroll
-            for (int dc = 0; dc < DC; ++dc) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(kb_ + k_rd[dc] + kb * 32 * ROWB);
-                st.v[kb] = Ops::mma(a, qreg[dc], st.v[kb]);
+                    for (int i = 0; i < 16; ++i) st.v[kb][b][i] = 0.f;
             }
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(kbuf + k_rd[dc] + kb * 32 * ROWB);
+#pragma unroll
+            for (int b = 0; b < QB; ++b) st.v[kb][b] = Ops::mma(a, qreg[b][dc], st.v[kb][b]);
         }
-        return st;
-    };
-    // masking, online softmax and O^T += V^T P^T for one tile
-    auto softmax_pv = [&](STile st, int k0, const uint8_t *vb_) {
-        if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + kb * 32 + (i >> 3) * 16 + hi * 8 + (i & 7);
-                    const bool keep = key < p.Lk && (!CAUSAL || key <= qw + l32);
-                    st.v[kb][i] = keep ? st.v[kb][i] : -INFINITY;
-                }
-        }
-        // four independent partial maxima / sums keep the dependency
-        // chains short
-        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], st.v[kb][i]);
-        const float mx = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-        const float m_new = fmaxf(m_run, mx);
-        if (__any((m_new - m_run) * c > kLazyThreshold)) {
-            const float alpha = (m_new == -INFINITY) ? 1.f
-                                                     : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-            m_run = m_new;
-            l_part *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        }
-        const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-        u32x4 pk[KC];
-        float r4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            float e[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                e[i] = __builtin_amdgcn_exp2f(fmaf(st.v[kb][i], c, -mc));
-                r4[i & 3] += e[i];
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                u32x4 x;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) x[w] = Ops::pack2(e[h * 8 + 2 * w], e[h * 8 + 2 * w + 1]);
-                pk[kb * 2 + h] = x;
-            }
-        }
-        l_part += (r4[0] + r4[1]) + (r4[2] + r4[3]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const uint8_t *vp = vb_ + v_rd[db] + kc * 16 * ROWB;
-                const uint2 lo = ds_read_tr(vp);
-                const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
-                const u32x4 a = {lo.x, lo.y, hi4.x, hi4.y};
-                oacc[db] = Ops::mma(a, pk[kc], oacc[db]);
-            }
     };
     auto sync_tiles = [&]() {
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
 
-    if constexpr (!SWP) {
-        // one tile per step: K_j and V_j are loaded together, one step ahead
-        issue_k(0, k_lds0);
-        issue_v(0, v_lds0);
-        sync_tiles();
-        for (int j = 0; j < ntiles; j += 2) {
-            if (j + 1 < ntiles) {
-                issue_k((j + 1) * BN, k_lds1);
-                issue_v((j + 1) * BN, v_lds1);
-            }
-            if (active(j * BN)) softmax_pv(qk(k_lds0), j * BN, v_lds0);
-            sync_tiles();
-            if (j + 1 >= ntiles) break;
-            if (j + 2 < ntiles) {
-                issue_k((j + 2) * BN, k_lds0);
-                issue_v((j + 2) * BN, v_lds0);
-            }
-            if (active((j + 1) * BN)) softmax_pv(qk(k_lds1), (j + 1) * BN, v_lds1);
-            sync_tiles();
-        }
-    } else {
-        // Software pipeline: step j runs the QK^T MFMAs of tile j+1 while
-        // the vector ALUs run the softmax of tile j, then adds P_j V_j.  K
-        // therefore runs one tile ahead of V: during step j the DMA fills
-        // K_{j+2} and V_{j+1}, into the buffers that K_j and V_{j-1} left at
-        // the end of step j-1.  Each step is branch-free apart from the DMA
-        // guards and the mask at its start and the rare rescale, and
-        // sched_group_barrier pins the MFMA / LDS-read / VALU interleave of
-        // the two straight-line blocks.  Tiles past a wave's diagonal are not
-        // skipped: they are fully masked and contribute p = 0.
-        // MFMAs of the next tile's QK^T issued before / after the rescale
-        // branch, and VALU slots given to each MFMA of the second half
-        constexpr int HALF = KB * DC / 2;
-        // per 8-key chunk of P: 8 FMA + 8 exp + 8 add + 4 convert
-        constexpr int VALU_P = 28;
-        constexpr int VALU_B = 2 * VALU_P / (KB * DC - HALF);
-        constexpr int VALU_C = (KC > 2 ? (KC - 2) * VALU_P : 0) / (DB * KC) + 1;
-        // With STAGES = 3 the DMA runs one more step ahead: step j fills
-        // K_{j+3} and V_{j+2}, and its closing wait covers only the loads of
-        // the step before (vmcnt counts the newer ones still in flight).
-        constexpr int AHEAD = STAGES - 1;
-        issue_k(0, k_lds0);
-        issue_v(0, v_lds0);
-        if (ntiles > 1) issue_k(BN, k_lds1);
-        sync_tiles();
-        if constexpr (STAGES == 3) {
-            if (ntiles > 2) issue_k(2 * BN, k_lds2);
-            if (ntiles > 1) issue_v(BN, v_lds1);
-        }
-        STile cur;
-        cur = qk(k_lds0);  // (assigned, not initialised: keeps clang from
-                           // trying to constant-fold the call)
-        __syncthreads();   // everyone is done with K_0 before the DMA refills it
+    // Software pipeline: step j runs the QK^T MFMAs of tile j+1 while the
+    // vector ALUs run the softmax of tile j, then adds P_j V_j.  K therefore
+    // runs one tile ahead of V: during step j the DMA fills K_{j+2} and
+    // V_{j+1}, into the buffers that K_j and V_{j-1} left at the end of step
+    // j-1.  Each step is branch-free apart from the DMA guards and the mask at
+    // its start and the rare rescale, and sched_group_barrier pins the MFMA /
+    // LDS-read / VALU interleave of the two straight-line blocks.  Tiles past
+    // a wave's diagonal are not skipped: they are fully masked and contribute
+    // p = 0.
+    issue_k(0, k_lds0);
+    issue_v(0, v_lds0);
+    if (ntiles > 1) issue_k(BN, k_lds1);
+    sync_tiles();
+    STile cur;
+    qk_part(cur, k_lds0, 0, NQK);
+    __syncthreads();   // everyone is done with K_0 before K_2 lands there
 
-        auto step = [&](int j, const uint8_t *k_next, const uint8_t *v_cur, uint8_t *k_dma,
-                        uint8_t *v_dma) {
-            const bool dma_k = j + AHEAD + 1 < ntiles;
-            const bool dma_v = j + AHEAD < ntiles;
-            if (dma_k) issue_k((j + AHEAD + 1) * BN, k_dma);
-            if (dma_v) issue_v((j + AHEAD) * BN, v_dma);
-            const int k0 = j * BN;
-            if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
+    // VALU slots per MFMA: one 8-key chunk of P costs 8 FMA + 8 exp + 8 add
+    // + 4 convert; chunks 0-1 go under the second half of QK^T, chunks
+    // 2..KC-1 under the PV MFMAs
+    constexpr int VALU_P = 28;
+    constexpr int VALU_B = (2 * VALU_P + HALF - 1) / HALF;
+    constexpr int VALU_C = ((KC - 2) * VALU_P + 4 + DB * KC - 1) / (DB * KC);
+
+    auto step = [&](int j, const uint8_t *k_next, const uint8_t *v_cur, uint8_t *k_dma,
+                    uint8_t *v_dma) {
+        if (j + 2 < ntiles) issue_k((j + 2) * BN, k_dma);
+        if (j + 1 < ntiles) issue_v((j + 1) * BN, v_dma);
+        const int k0 = j * BN;
+        if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int b = 0; b < QB; ++b)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int key = k0 + kb * 32 + (i >> 3) * 16 + hi * 8 + (i & 7);
-                        const bool keep = key < p.Lk && (!CAUSAL || key <= qw + l32);
-                        cur.v[kb][i] = keep ? cur.v[kb][i] : -INFINITY;
+                        const bool keep = key < p.Lk && (!CAUSAL || key <= qw + b * 32 + l32);
+                        cur.v[kb][b][i] = keep ? cur.v[kb][b][i] : -INFINITY;
                     }
-            }
-            // block A: row max of tile j | first half of QK^T for tile j+1
-            STile nxt;
+        }
+        // block A: row maxima of tile j | first half of QK^T for tile j+1
+        STile nxt;
+        float mx[QB];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            // four independent partial maxima keep the chains short
             float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], cur.v[kb][i]);
+                for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], cur.v[kb][b][i]);
+            mx[b] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        }
+        qk_part(nxt, k_next, 0, HALF);
+        float m_new[QB];
+        bool grow = false;
 #pragma unroll
-            for (int n = 0; n < HALF; ++n) {
-                const int kb = n / DC, dc = n % DC;
-                if (dc == 0) {
+        for (int b = 0; b < QB; ++b) {
+            m_new[b] = fmaxf(m_run[b], half_max(mx[b]));
+            grow = grow || (m_new[b] - m_run[b]) * c > kLazyThreshold;
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);            // LDS read
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) nxt.v[kb][i] = 0.f;
-                }
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(k_next + k_rd[dc] + kb * 32 * ROWB);
-                nxt.v[kb] = Ops::mma(a, qreg[dc], nxt.v[kb]);
-            }
-            const float mx = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-            const float m_new = fmaxf(m_run, mx);
-            const bool grow = (m_new - m_run) * c > kLazyThreshold;
-            // LDS reads run three MFMAs ahead of their use
-            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);       // LDS read
+        for (int n = 0; n < HALF; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);       // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 2 * QB, 0);   // VALU
+        }
+        if (__any(grow)) {
 #pragma unroll
-            for (int n = 0; n < HALF; ++n) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
-            }
-            if (__any(grow)) {
-                const float alpha = (m_new == -INFINITY)
+            for (int b = 0; b < QB; ++b) {
+                // m_run = -inf gives alpha = 0 (nothing accumulated yet)
+                const float alpha = (m_new[b] == -INFINITY)
                                         ? 1.f
-                                        : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-                m_run = m_new;
-                l_part *= alpha;
+                                        : __builtin_amdgcn_exp2f((m_run[b] - m_new[b]) * c);
+                m_run[b] = m_new[b];
+                l_part[b] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-            }
-            // block B: second half of QK^T for tile j+1 under the
-            // exponentials of key chunks 0-1 of tile j; then O^T += V^T P^T
-            // chunk by chunk, with the exponentials of chunks 2-3 under the
-            // PV MFMAs of chunks 0-1.  That keeps MFMA and VALU work
-            // balanced inside each phase.
-            const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-            float r4[4] = {0.f, 0.f, 0.f, 0.f};
-            auto make_p = [&](int kc) {
-                const int kb = kc >> 1, h = kc & 1;
-                float e[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    e[i] = __builtin_amdgcn_exp2f(fmaf(cur.v[kb][h * 8 + i], c, -mc));
-                    r4[i & 3] += e[i];
-                }
-                u32x4 x;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) x[w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
-                return x;
-            };
-            u32x4 pk[KC];
-            pk[0] = make_p(0);
-            pk[1] = make_p(1);
-#pragma unroll
-            for (int n = HALF; n < KB * DC; ++n) {
-                const int kb = n / DC, dc = n % DC;
-                if (dc == 0) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) nxt.v[kb][i] = 0.f;
-                }
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(k_next + k_rd[dc] + kb * 32 * ROWB);
-                nxt.v[kb] = Ops::mma(a, qreg[dc], nxt.v[kb]);
-            }
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                if (kc + 2 < KC) pk[kc + 2] = make_p(kc + 2);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const uint8_t *vp = v_cur + v_rd[db] + kc * 16 * ROWB;
-                    const uint2 lo = ds_read_tr(vp);
-                    const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
-                    const u32x4 a = {lo.x, lo.y, hi4.x, hi4.y};
-                    oacc[db] = Ops::mma(a, pk[kc], oacc[db]);
-                }
-            }
-            l_part += (r4[0] + r4[1]) + (r4[2] + r4[3]);
-            // K reads three MFMAs ahead; the transposed V reads stay two PV
-            // MFMAs ahead
-            __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);            // LDS read
-#pragma unroll
-            for (int n = HALF; n < KB * DC; ++n) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);        // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);        // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, VALU_B, 1);   // VALU
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);            // LDS read
-#pragma unroll
-            for (int n = 0; n < DB * KC; ++n) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);        // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);        // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, VALU_C, 1);   // VALU
-            }
-            cur = nxt;
-            if constexpr (STAGES == 3) {
-                // wait for the previous step's loads only
-                if (dma_k && dma_v) wait_vmcnt<2 * LOADS>();
-                else if (dma_k || dma_v) wait_vmcnt<LOADS>();
-                else wait_vmcnt<0>();
-                __syncthreads();
-            } else {
-                sync_tiles();
-            }
-        };
-        if constexpr (STAGES == 3) {
-            for (int j = 0; j < ntiles; j += 3) {
-                step(j, k_lds1, v_lds0, k_lds0, v_lds2);
-                if (j + 1 >= ntiles) break;
-                step(j + 1, k_lds2, v_lds1, k_lds1, v_lds0);
-                if (j + 2 >= ntiles) break;
-                step(j + 2, k_lds0, v_lds2, k_lds2, v_lds1);
-            }
-        } else {
-            for (int j = 0; j < ntiles; j += 2) {
-                step(j, k_lds1, v_lds0, k_lds0, v_lds1);
-                if (j + 1 >= ntiles) break;
-                step(j + 1, k_lds0, v_lds1, k_lds1, v_lds0);
+                    for (int i = 0; i < 16; ++i) oacc[db][b][i] *= alpha;
             }
         }
+        // block B: second half of QK^T for tile j+1 under the exponentials of
+        // key chunks 0-1 of tile j; then O^T += V^T P^T chunk by chunk, with
+        // the exponentials of the later chunks under the PV MFMAs of the
+        // earlier ones.  That keeps MFMA and VALU work balanced inside each
+        // phase.
+        float mc[QB], r4[QB][4];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            mc[b] = (m_run[b] == -INFINITY) ? 0.f : m_run[b] * c;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) r4[b][w] = 0.f;
+        }
+        auto make_p = [&](int kc, int b) {
+            const int kb = kc >> 1, h = kc & 1;
+            float e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                e[i] = __builtin_amdgcn_exp2f(fmaf(cur.v[kb][b][h * 8 + i], c, -mc[b]));
+                r4[b][i & 3] += e[i];
+            }
+            u32x4 x;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) x[w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
+            return x;
+        };
+        u32x4 pk[KC][QB];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            pk[0][b] = make_p(0, b);
+            pk[1][b] = make_p(1, b);
+        }
+        qk_part(nxt, k_next, HALF, NQK);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            if (kc + 2 < KC) {
+#pragma unroll
+                for (int b = 0; b < QB; ++b) pk[kc + 2][b] = make_p(kc + 2, b);
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const uint8_t *vp = v_cur + v_rd[db] + kc * 16 * ROWB;
+                const uint2 lo = ds_read_tr(vp);
+                const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
+                const u32x4 a = {lo.x, lo.y, hi4.x, hi4.y};
+#pragma unroll
+                for (int b = 0; b < QB; ++b) oacc[db][b] = Ops::mma(a, pk[kc][b], oacc[db][b]);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < QB; ++b) l_part[b] += (r4[b][0] + r4[b][1]) + (r4[b][2] + r4[b][3]);
+        // K reads two MFMA groups ahead; the transposed V reads stay ahead of
+        // the PV MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);                 // LDS read
+#pragma unroll
+        for (int n = HALF; n < NQK; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, QB, 1);            // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);             // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, VALU_B * QB, 1);   // VALU
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);                 // LDS read
+#pragma unroll
+        for (int n = 0; n < DB * KC; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, QB, 1);            // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);             // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, VALU_C * QB, 1);   // VALU
+        }
+        cur = nxt;
+        sync_tiles();
+    };
+    for (int j = 0; j < ntiles; j += 2) {
+        step(j, k_lds1, v_lds0, k_lds0, v_lds1);
+        if (j + 1 >= ntiles) break;
+        step(j + 1, k_lds0, v_lds1, k_lds1, v_lds0);
     }
 
-    // ---- epilogue
-    const float l = half_sum(l_part);
-    const int row = qw + l32;
-    if (row < p.Lq) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t *orow = p.o + ((int64_t)bh * p.Lq + row) * D;
+    // ---- epilogue: O = acc / l, rounded to nearest even; LSE = m*scale + ln l
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int b = 0; b < QB; ++b) {
+        const float l = half_sum(l_part[b]);
+        const int row = qw + b * 32 + l32;
+        if (row < p.Lq) {
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            uint16_t *orow = p.o + ((int64_t)bh * p.Lq + row) * D;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = db * 32 + g * 8 + hi * 4;
-                u32x2 x = {Ops::pack2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                           Ops::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-                *reinterpret_cast<u32x2 *>(orow + d) = x;
-            }
-        if (p.lse != nullptr && hi == 0)
-            p.lse[(int64_t)bh * p.Lq + row] = l > 0.f ? m_run * p.scale + __logf(l) : -INFINITY;
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d = db * 32 + g * 8 + hi * 4;
+                    u32x2 x = {Ops::pack2(oacc[db][b][4 * g] * inv, oacc[db][b][4 * g + 1] * inv),
+                               Ops::pack2(oacc[db][b][4 * g + 2] * inv, oacc[db][b][4 * g + 3] * inv)};
+                    *reinterpret_cast<u32x2 *>(orow + d) = x;
+                }
+            if (p.lse != nullptr && hi == 0)
+                p.lse[(int64_t)bh * p.Lq + row] =
+                    l > 0.f ? m_run[b] * p.scale + __logf(l) : -INFINITY;
+        }
     }
 }
 
-template <typename Ops, int D, bool CAUSAL, int NW, int BN, int OCC, bool SWP, int STAGES>
+template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN, int OCC>
 hipError_t launch_dma(const FwdArgs &a)
 {
-    constexpr int BM = NW * 32;
+    constexpr int BM = NW * QB * 32;
     Params p;
     p.q = static_cast<const uint16_t *>(a.q);
     p.k = static_cast<const uint16_t *>(a.k);
@@ -926,7 +834,7 @@ hipError_t launch_dma(const FwdArgs &a)
     p.scale = a.scale;
     p.c = a.scale * kLog2e;
     const int64_t nwg = (int64_t)p.BH * p.ntq;
-    hipLaunchKernelGGL((fa_fwd_mfma_dma_kernel<Ops, D, CAUSAL, NW, BN, OCC, SWP, STAGES>),
+    hipLaunchKernelGGL((fa_fwd_mfma_dma_kernel<Ops, D, CAUSAL, NW, QB, BN, OCC>),
                        dim3((unsigned)nwg), dim3(NW * 64), 0, a.stream, p);
     return hipGetLastError();
 }
@@ -967,27 +875,22 @@ hipError_t launch_tile(const FwdArgs &a, const MfmaTile &t)
     return hipErrorInvalidConfiguration;
 }
 
-template <typename Ops, int D, bool CAUSAL, int NW, int BN, int OCC>
-hipError_t launch_pipe(const FwdArgs &a, int pipe)
-{
-    if (pipe == 1) return launch_dma<Ops, D, CAUSAL, NW, BN, OCC, false, 2>(a);
-    if (pipe == 2) return launch_dma<Ops, D, CAUSAL, NW, BN, OCC, true, 2>(a);
-    return launch_dma<Ops, D, CAUSAL, NW, BN, OCC, true, 3>(a);
-}
-
 template <typename Ops, int D, bool CAUSAL>
 hipError_t launch_tile_dma(const FwdArgs &a, const MfmaTile &t)
 {
-    if (t.qb != 1) return hipErrorInvalidConfiguration;
-    if (t.nw == 8 && t.bn == 64 && t.occ == 2) return launch_pipe<Ops, D, CAUSAL, 8, 64, 2>(a, t.pipe);
-    if (t.nw == 4 && t.bn == 64 && t.occ == 2) return launch_pipe<Ops, D, CAUSAL, 4, 64, 2>(a, t.pipe);
+    if (t.nw == 8 && t.qb == 1 && t.bn == 64 && t.occ == 2)
+        return launch_dma<Ops, D, CAUSAL, 8, 1, 64, 2>(a);
+    if (t.nw == 4 && t.qb == 1 && t.bn == 64 && t.occ == 2)
+        return launch_dma<Ops, D, CAUSAL, 4, 1, 64, 2>(a);
+    if (t.nw == 4 && t.qb == 2 && t.bn == 64 && t.occ == 1)
+        return launch_dma<Ops, D, CAUSAL, 4, 2, 64, 1>(a);
     return hipErrorInvalidConfiguration;
 }
 
 template <typename Ops>
 hipError_t launch_ops(const FwdArgs &a, const MfmaTile &t)
 {
-    if (t.pipe >= 1 && t.pipe <= 3) {
+    if (t.pipe == 2) {
         if (a.D == 64)
             return a.causal ? launch_tile_dma<Ops, 64, true>(a, t)
                             : launch_tile_dma<Ops, 64, false>(a, t);
