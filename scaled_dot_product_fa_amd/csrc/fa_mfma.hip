@@ -478,6 +478,25 @@ __device__ __forceinline__ uint2 ds_read_tr(const uint8_t *p)
     return __builtin_bit_cast(uint2, r);
 }
 
+// One global_load_lds_dwordx4: the wave's 64 lanes each fetch 16 bytes from
+// their own global address and the hardware writes them to LDS at m0 +
+// 16 * lane.  Issued from inline assembly on purpose: the compiler treats
+// its own LDS-DMA instruction as a FLAT access that may target LDS, and while
+// one is in flight it then waits for every outstanding LDS read (lgkmcnt(0))
+// before each use of any of them, which exposes the full LDS latency on every
+// MFMA operand.  Hidden from the compiler, the DMA only counts against
+// vmcnt, and the kernel orders it with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void dma_16B(const void *src, uint32_t lds_dst)
+{
+    __asm__ volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_dst) : "memory");
+}
+
+// LDS byte address of a __shared__ object (for m0).
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -503,8 +522,8 @@ void fa_fwd_mfma_dma_kernel(Params p)
     static_assert(LOADS >= 1 && TILEB % (NT * 16) == 0, "tile split");
     static_assert(BN % 32 == 0 && D % 32 == 0 && KC >= 2, "tile shape");
 
-    // Two buffers per operand as distinct objects, so the compiler can tell
-    // the DMA into one buffer from the reads of the other.
+    // Two buffers per operand (separate objects; the DMA into one overlaps
+    // the reads of the other).
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILEB];
@@ -549,10 +568,13 @@ void fa_fwd_mfma_dma_kernel(Params p)
     }
     auto issue_one = [&](const uint16_t *src, const uint32_t *offs, int k0, uint8_t *dst) {
         const uint8_t *t = reinterpret_cast<const uint8_t *>(src + (int64_t)k0 * D);
+        // wave-uniform LDS base of this wave's 1 KB slots (an SGPR)
+        const uint32_t dbase = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(lds_addr(dst) + (uint32_t)(wave * 1024)));
         if (k0 + BN <= p.Lk) {   // uniform: every row of the tile exists
 #pragma unroll
             for (int r = 0; r < LOADS; ++r)
-                __builtin_amdgcn_global_load_lds(t + offs[r], dst + (r * NW + wave) * 1024, 16, 0, 0);
+                dma_16B(t + offs[r], dbase + (uint32_t)(r * NW * 1024));
             return;
         }
         const int last = p.Lk - 1 - k0;  // last valid row of this tile
@@ -564,7 +586,7 @@ void fa_fwd_mfma_dma_kernel(Params p)
                 // are masked and its V rows get probability 0)
                 o -= (uint32_t)(ld_row[r] - last) * ROWB;
             }
-            __builtin_amdgcn_global_load_lds(t + o, dst + (r * NW + wave) * 1024, 16, 0, 0);
+            dma_16B(t + o, dbase + (uint32_t)(r * NW * 1024));
         }
     };
     auto issue_k = [&](int k0, uint8_t *kd) { issue_one(kh, ld_k, k0, kd); };
