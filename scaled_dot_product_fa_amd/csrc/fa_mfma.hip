@@ -42,6 +42,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -54,6 +56,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+#ifndef PP_LEAD
+#define PP_LEAD 4
+#endif
+
 
 constexpr float kLog2e = 1.4426950408889634f;
 // The running max is only raised when it grew by more than this many binary
@@ -491,6 +498,14 @@ __device__ __forceinline__ void dma_16B(const void *src, uint32_t lds_dst)
     __asm__ volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_dst) : "memory");
 }
 
+// The same load with a wave-uniform 64-bit base (SGPRs) and a per-lane
+// 32-bit byte offset.  No memory clobber: the loads target LDS buffers that
+// no wave reads before the next barrier, so LDS reads may move across them.
+__device__ __forceinline__ void dma_16B_sbase(const void *base, uint32_t off, uint32_t lds_dst)
+{
+    __asm__ volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_dst));
+}
+
 // LDS byte address of a __shared__ object (for m0).
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
@@ -839,6 +854,372 @@ void fa_fwd_mfma_dma_kernel(Params p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong variant (8 waves, 32 query rows each, 64-key tiles).  The two
+// waves that share a SIMD (w and w + 4) run half a step apart: while one
+// issues the MFMAs of its step (P_j V_j for tile j and S_{j+1} = Q K_{j+1}^T
+// for the next tile, reading K and V from LDS), the other runs the softmax
+// of its next tile on the vector ALU, and a workgroup barrier after every
+// phase keeps the two groups in this alternation.  One "slot" is the time
+// between two barriers; group 0 (waves 0-3) runs its MFMA phases in even
+// slots and group 1 (waves 4-7) in odd slots:
+//   group 0: QK_0 | SM_0 | PV_0+QK_1 | SM_1 | PV_1+QK_2 | ...
+//   group 1:  --  | QK_0 | SM_0      | PV_0+QK_1 | SM_1 | ...
+// so K_t is read in slots 2t and 2t+1 and V_t in slots 2t+2 and 2t+3.
+// Every slot loads one tile, in pieces spread through both phases so that
+// no wave stalls behind a burst of loads: slot 2s loads K_{s+1} (two K
+// buffers) and slot 2s+1 loads V_{s+1} (three V buffers).  A wave waits for
+// its loads of the previous slot and the one before (vmcnt) before the
+// barrier that ends each odd slot.
+// ---------------------------------------------------------------------------
+template <typename Ops, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_mfma_pp_kernel(Params p)
+{
+    constexpr int NW = 8, BN = 64;
+    constexpr int BM = NW * 32;          // query rows per workgroup
+    constexpr int DC = D / 16;           // 16-dim chunks (k of the QK^T MFMA)
+    constexpr int DB = D / 32;           // 32-dim blocks (rows of O^T)
+    constexpr int KB = BN / 32;          // 32-key blocks (rows of S^T)
+    constexpr int KC = BN / 16;          // 16-key chunks (k of the PV MFMA)
+    constexpr int ROWB = D * 2;          // bytes per K or V row in LDS
+    constexpr int KCH = D / 8;           // 16-byte chunks per row
+    constexpr int TILEB = BN * ROWB;     // bytes of one K (or V) tile
+    constexpr int LOADS = TILEB / (NW * 64 * 16);   // loads per wave per tile
+    static_assert(LOADS >= 1 && TILEB % (NW * 64 * 16) == 0, "tile split");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds[2][TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds[4][TILEB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;           // waves w and w+4 share a SIMD
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    int bh, qt;
+    decompose(blockIdx.x, gridDim.x, p.BH, p.ntq, CAUSAL, bh, qt);
+    const int q_first = qt * BM;
+    const int qw = q_first + wave * 32;   // first query row of this wave
+    const int qrow = qw + l32;            // this lane's query row
+
+    const uint16_t *qh = p.q + (int64_t)bh * p.Lq * D;
+    const uint16_t *kh = p.k + (int64_t)bh * p.Lk * D;
+    const uint16_t *vh = p.v + (int64_t)bh * p.Lk * D;
+
+    // ---- Q^T operand in VGPRs (rows past Lq read the last row; not stored)
+    u32x4 qreg[DC];
+    {
+        const int row = min(qrow, p.Lq - 1);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+            qreg[dc] = *reinterpret_cast<const u32x4 *>(qh + (uint32_t)row * D + dc * 16 + hi * 8);
+    }
+
+    const int kv_end = CAUSAL ? min(p.Lk, q_first + BM) : p.Lk;
+    const int ntiles = (kv_end + BN - 1) / BN;
+
+    // ---- loads: per-lane source offsets (bytes within a tile)
+    // (V offset, and K minus V offset: the per-load choice between K and V
+    // is then a select against zero, which stays in registers)
+    int ld_row[LOADS];
+    uint32_t ld_v[LOADS], ld_kv[LOADS];
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+        const int slot = (r * NW + wave) * 64 + lane;
+        const int row = slot / KCH, pc = slot % KCH;
+        ld_row[r] = row;
+        ld_v[r] = (uint32_t)(row * D + (pc ^ swz_v<D>(row)) * 8) * 2;
+        ld_kv[r] = (uint32_t)(row * D + (pc ^ swz_k<D>(row)) * 8) * 2 - ld_v[r];
+    }
+    const uint32_t k_base = lds_addr(k_lds[0]), v_base = lds_addr(v_lds[0]);
+    // The loads of one phase, worked out before its straight-line block: the
+    // tile's global base, the LDS destination of this wave's first piece and
+    // the per-lane byte offsets.  K tiles go to buffer tile % 2, V tiles to
+    // buffer tile % 4.  Past the last tile the last tile is fetched again
+    // (into the buffer of the requested tile, which no wave reads any more),
+    // so every slot issues the same loads; rows past the end of the keys
+    // fetch the last valid row (their scores are masked and their V rows get
+    // probability 0).
+    struct LoadPlan {
+        const uint16_t *src;
+        uint32_t dst;
+        uint32_t off[LOADS];
+    };
+    auto plan = [&](bool is_k, int tile) {
+        LoadPlan pl;
+        const int k0 = min(tile, ntiles - 1) * BN;
+        pl.src = (is_k ? kh : vh) + (int64_t)k0 * D;
+        pl.dst = (is_k ? k_base + (uint32_t)((tile & 1) * TILEB)
+                       : v_base + (uint32_t)((tile & 3) * TILEB)) +
+                 (uint32_t)(wave * 1024);
+        const int last = p.Lk - 1 - k0;
+#pragma unroll
+        for (int r = 0; r < LOADS; ++r)
+            pl.off[r] = ld_v[r] + (is_k ? ld_kv[r] : 0u) -
+                        (uint32_t)(max(ld_row[r] - last, 0) * ROWB);
+        return pl;
+    };
+    auto issue = [&](const LoadPlan &pl, int r) {
+        dma_16B_sbase(pl.src, pl.off[r], pl.dst + (uint32_t)(r * NW * 1024));
+    };
+
+    // ---- per-lane LDS read offsets (loop invariant)
+    uint32_t k_rd[DC];
+    {
+        const int row = swap_bits23(l32);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+            k_rd[dc] = (uint32_t)(row * ROWB + (((dc * 2 + hi) ^ swz_k<D>(row)) * 16));
+    }
+    uint32_t v_rd[DB];
+    {
+        const int g = lane >> 4, t = lane & 15;
+        const int row = 8 * hi + (t >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + 16 * (g & 1) + 4 * (t & 3);   // element
+            const int c = col >> 3, within = (col & 7) * 2;
+            v_rd[db] = (uint32_t)(row * ROWB + ((c ^ swz_v<D>(row)) * 16) + within);
+        }
+    }
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float m_run = -INFINITY, l_part = 0.f;
+    const float c = p.c;
+
+    f32x16 st[KB];    // S^T of the tile whose softmax runs next
+    u32x4 pk[KC];     // P^T (I/O type) of the tile whose PV runs next
+
+    // S^T = K Q^T for one tile: A = 32 keys x 16 dims of K (LDS), B = Q^T.
+    auto qk_mma = [&](const uint8_t *kbuf, int dc, int kb) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(kbuf + k_rd[dc] + kb * 32 * ROWB);
+        if (dc == 0) {
+            f32x16 z;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) z[i] = 0.f;
+            st[kb] = Ops::mma(a, qreg[0], z);
+        } else {
+            st[kb] = Ops::mma(a, qreg[dc], st[kb]);
+        }
+    };
+    // One MFMA phase in slot t: O^T += V^T P^T for tile j (A = 32 dims x 16
+    // keys of V from two transposed LDS reads, B = P^T), then S^T = K Q^T for
+    // tile j+1.  The last tile's phase also runs the QK^T half, on whatever
+    // the K buffer holds (the result is never used), so that every phase is
+    // one straight-line block.  LDS reads are pinned PP_LEAD MFMAs ahead of
+    // their use; the slot's loads go out after the first PV MFMAs and the
+    // first QK^T MFMAs.
+    constexpr int NPV = KC * DB, NQK = DC * KB;
+    auto mfma_phase = [&](const LoadPlan &pl, const uint8_t *vbuf, const uint8_t *kbuf) {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const uint8_t *vp = vbuf + v_rd[db] + kc * 16 * ROWB;
+                const uint2 lo = ds_read_tr(vp);
+                const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
+                oacc[db] = Ops::mma(u32x4{lo.x, lo.y, hi4.x, hi4.y}, pk[kc], oacc[db]);
+                if (kc == 1 && db == 0) issue(pl, 0);
+            }
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                qk_mma(kbuf, dc, kb);
+                if (LOADS > 1 && dc == 1 && kb == 0) issue(pl, LOADS - 1);
+            }
+        constexpr int LEAD = PP_LEAD;
+        constexpr int NM = NPV + NQK;
+        static_assert(LEAD >= 1 && LEAD <= NPV, "read lead");
+        // MFMA n (n < NPV: PV, else QK) is preceded by the reads of MFMA n + LEAD
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
+#pragma unroll
+        for (int n = 0; n < NPV - LEAD; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int n = NPV - LEAD; n < NM - LEAD; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
+        // S must exist before the barrier
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) __asm__ volatile("" : "+v"(st[kb]));
+    };
+    // Online softmax of tile j in slot t (vector ALU only): mask, row max,
+    // lazy rescale, p = exp2(s*c - m*c) rounded to the I/O type, row sum.
+    auto softmax = [&](const LoadPlan &pl, int j) {
+        issue(pl, 0);
+        const int k0 = j * BN;
+        if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = k0 + kb * 32 + (i >> 3) * 16 + hi * 8 + (i & 7);
+                    const bool keep = key < p.Lk && (!CAUSAL || key <= qrow);
+                    st[kb][i] = keep ? st[kb][i] : -INFINITY;
+                }
+        }
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], st[kb][i]);
+        const float mx = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+        const float m_new = fmaxf(m_run, mx);
+        if (__any((m_new - m_run) * c > kLazyThreshold)) {
+            // m_run = -inf gives alpha = 0 (nothing accumulated yet)
+            const float alpha =
+                (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+            m_run = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        }
+        const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+        float r4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            if (LOADS > 1 && kc == KC / 2) issue(pl, LOADS - 1);
+            const int kb = kc >> 1, h = kc & 1;
+            float e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                e[i] = __builtin_amdgcn_exp2f(fmaf(st[kb][h * 8 + i], c, -mc));
+                r4[i & 3] += e[i];
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) pk[kc][w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
+        }
+        l_part += (r4[0] + r4[1]) + (r4[2] + r4[3]);
+        // P must exist before the barrier
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) __asm__ volatile("" : "+v"(pk[kc]));
+    };
+    static_assert(LOADS <= 2, "two load points per phase");
+    // End of slot t: odd slots first wait for all but this slot's loads
+    // (so K_{s+1} and V_s have landed), then every slot ends in a barrier.
+    // Group 1 ends on an MFMA phase in slot 2*ntiles + 1, after which no
+    // barrier is needed.
+    const int last_slot = 2 * ntiles + 1;
+    auto slot_end = [&](int t) {
+        if (t & 1) wait_vmcnt<LOADS>();
+        if (t != last_slot) __syncthreads();
+    };
+
+    // Loads per slot: group 0 runs SM_j in slot 2j+1 (loads V_{j+1}) and
+    // PV_j+QK_{j+1} in slot 2j+2 (loads K_{j+2}); group 1 runs SM_j in slot
+    // 2j+2 (K_{j+2}) and PV_j+QK_{j+1} in slot 2j+3 (V_{j+2}).
+    {
+        const LoadPlan k0p = plan(true, 0), v0p = plan(false, 0);
+#pragma unroll
+        for (int r = 0; r < LOADS; ++r) {
+            issue(k0p, r);
+            issue(v0p, r);
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    int t = 0;
+    if (grp == 1) {   // group 1 starts one slot late, loading its share of K_1
+        const LoadPlan pl = plan(true, 1);
+#pragma unroll
+        for (int r = 0; r < LOADS; ++r) issue(pl, r);
+        slot_end(t);
+        ++t;
+    }
+    {   // S^T of tile 0 (loads K_1 in group 0's slot 0, V_1 in group 1's slot 1)
+        const LoadPlan pl = plan(grp == 0, 1);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) qk_mma(k_lds[0], dc, kb);
+#pragma unroll
+        for (int r = 0; r < LOADS; ++r) issue(pl, r);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) __asm__ volatile("" : "+v"(st[kb]));
+        slot_end(t);
+        ++t;
+    }
+    // unrolled by four so that every LDS read address is a constant offset
+    auto tile = [&](int j, const uint8_t *vbuf, const uint8_t *kbuf) {
+        {
+            const LoadPlan pl = plan(grp == 1, j + 1 + grp);
+            softmax(pl, j);
+            slot_end(t);
+            ++t;
+        }
+        {
+            const LoadPlan pl = plan(grp == 0, j + 2);
+            mfma_phase(pl, vbuf, kbuf);
+            slot_end(t);
+            ++t;
+        }
+    };
+    for (int j = 0; j < ntiles; j += 4) {
+        tile(j, v_lds[0], k_lds[1]);
+        if (j + 1 >= ntiles) break;
+        tile(j + 1, v_lds[1], k_lds[0]);
+        if (j + 2 >= ntiles) break;
+        tile(j + 2, v_lds[2], k_lds[1]);
+        if (j + 3 >= ntiles) break;
+        tile(j + 3, v_lds[3], k_lds[0]);
+    }
+    // no load may still be writing LDS when the workgroup ends
+    wait_vmcnt<0>();
+
+    // ---- epilogue: O = acc / l, rounded to nearest even; LSE = m*scale + ln l
+    const float l = half_sum(l_part);
+    if (qrow < p.Lq) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t *orow = p.o + ((int64_t)bh * p.Lq + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = db * 32 + g * 8 + hi * 4;
+                u32x2 x = {Ops::pack2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                           Ops::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(orow + d) = x;
+            }
+        if (p.lse != nullptr && hi == 0)
+            p.lse[(int64_t)bh * p.Lq + qrow] = l > 0.f ? m_run * p.scale + __logf(l) : -INFINITY;
+    }
+}
+
+template <typename Ops, int D, bool CAUSAL>
+hipError_t launch_pp(const FwdArgs &a)
+{
+    constexpr int BM = 256;
+    Params p;
+    p.q = static_cast<const uint16_t *>(a.q);
+    p.k = static_cast<const uint16_t *>(a.k);
+    p.v = static_cast<const uint16_t *>(a.v);
+    p.o = static_cast<uint16_t *>(a.o);
+    p.lse = a.lse;
+    p.BH = (int)(a.B * a.H);
+    p.Lq = (int)a.Lq;
+    p.Lk = (int)a.Lk;
+    p.ntq = (int)((a.Lq + BM - 1) / BM);
+    p.scale = a.scale;
+    p.c = a.scale * kLog2e;
+    const int64_t nwg = (int64_t)p.BH * p.ntq;
+    hipLaunchKernelGGL((fa_fwd_mfma_pp_kernel<Ops, D, CAUSAL>), dim3((unsigned)nwg), dim3(512),
+                       0, a.stream, p);
+    return hipGetLastError();
+}
+
 template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN, int OCC>
 hipError_t launch_dma(const FwdArgs &a)
 {
@@ -912,6 +1293,13 @@ hipError_t launch_tile_dma(const FwdArgs &a, const MfmaTile &t)
 template <typename Ops>
 hipError_t launch_ops(const FwdArgs &a, const MfmaTile &t)
 {
+    if (t.pipe == 3) {
+        if (!(t.nw == 8 && t.qb == 1 && t.bn == 64 && t.occ == 2))
+            return hipErrorInvalidConfiguration;
+        if (a.D == 64)
+            return a.causal ? launch_pp<Ops, 64, true>(a) : launch_pp<Ops, 64, false>(a);
+        return a.causal ? launch_pp<Ops, 128, true>(a) : launch_pp<Ops, 128, false>(a);
+    }
     if (t.pipe == 2) {
         if (a.D == 64)
             return a.causal ? launch_tile_dma<Ops, 64, true>(a, t)
