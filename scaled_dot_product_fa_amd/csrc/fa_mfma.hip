@@ -60,6 +60,12 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #ifndef PP_LEAD
 #define PP_LEAD 4
 #endif
+#ifndef PP_PRE
+#define PP_PRE 2
+#endif
+#ifndef PP_PRIO
+#define PP_PRIO 1
+#endif
 
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -867,10 +873,11 @@ void fa_fwd_mfma_dma_kernel(Params p)
 //   group 1:  --  | QK_0 | SM_0      | PV_0+QK_1 | SM_1 | ...
 // so K_t is read in slots 2t and 2t+1 and V_t in slots 2t+2 and 2t+3.
 // Every slot loads one tile, in pieces spread through both phases so that
-// no wave stalls behind a burst of loads: slot 2s loads K_{s+1} (two K
-// buffers) and slot 2s+1 loads V_{s+1} (three V buffers).  A wave waits for
-// its loads of the previous slot and the one before (vmcnt) before the
-// barrier that ends each odd slot.
+// no wave stalls behind a burst of loads: slot 2s loads V_{s+1} and slot
+// 2s+1 loads K_{s+2}, three LDS buffers each.  Before each barrier a wave
+// waits for its loads of all earlier slots (vmcnt), so the tiles an MFMA
+// phase reads are visible one slot early and the softmax phase before it
+// prefetches the phase's first V operands into registers.
 // ---------------------------------------------------------------------------
 template <typename Ops, int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -888,8 +895,8 @@ void fa_fwd_mfma_pp_kernel(Params p)
     constexpr int LOADS = TILEB / (NW * 64 * 16);   // loads per wave per tile
     static_assert(LOADS >= 1 && TILEB % (NW * 64 * 16) == 0, "tile split");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t k_lds[2][TILEB];
-    __shared__ __attribute__((aligned(1024))) uint8_t v_lds[4][TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds[3][TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds[3][TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -936,8 +943,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
     const uint32_t k_base = lds_addr(k_lds[0]), v_base = lds_addr(v_lds[0]);
     // The loads of one phase, worked out before its straight-line block: the
     // tile's global base, the LDS destination of this wave's first piece and
-    // the per-lane byte offsets.  K tiles go to buffer tile % 2, V tiles to
-    // buffer tile % 4.  Past the last tile the last tile is fetched again
+    // the per-lane byte offsets.  Tile t goes to buffer t % 3.  Past the last tile the last tile is fetched again
     // (into the buffer of the requested tile, which no wave reads any more),
     // so every slot issues the same loads; rows past the end of the keys
     // fetch the last valid row (their scores are masked and their V rows get
@@ -951,8 +957,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
         LoadPlan pl;
         const int k0 = min(tile, ntiles - 1) * BN;
         pl.src = (is_k ? kh : vh) + (int64_t)k0 * D;
-        pl.dst = (is_k ? k_base + (uint32_t)((tile & 1) * TILEB)
-                       : v_base + (uint32_t)((tile & 3) * TILEB)) +
+        pl.dst = (is_k ? k_base : v_base) + (uint32_t)((tile % 3) * TILEB) +
                  (uint32_t)(wave * 1024);
         const int last = p.Lk - 1 - k0;
 #pragma unroll
@@ -1008,23 +1013,32 @@ void fa_fwd_mfma_pp_kernel(Params p)
             st[kb] = Ops::mma(a, qreg[dc], st[kb]);
         }
     };
-    // One MFMA phase in slot t: O^T += V^T P^T for tile j (A = 32 dims x 16
-    // keys of V from two transposed LDS reads, B = P^T), then S^T = K Q^T for
-    // tile j+1.  The last tile's phase also runs the QK^T half, on whatever
-    // the K buffer holds (the result is never used), so that every phase is
-    // one straight-line block.  LDS reads are pinned PP_LEAD MFMAs ahead of
-    // their use; the slot's loads go out after the first PV MFMAs and the
-    // first QK^T MFMAs.
+    // One MFMA phase: O^T += V^T P^T for tile j (A = 32 dims x 16 keys of V
+    // from two transposed LDS reads, B = P^T), then S^T = K Q^T for tile j+1.
+    // The first NPRE V operands were read during the softmax phase before.
+    // The last tile's phase also runs the QK^T half, on whatever the K
+    // buffer holds (the result is never used), so that every phase is one
+    // straight-line block.  The other LDS reads are pinned PP_LEAD MFMAs
+    // ahead of their use; the slot's loads go out after the first PV MFMAs
+    // and the first QK^T MFMAs.
     constexpr int NPV = KC * DB, NQK = DC * KB;
+    constexpr int NPRE = PP_PRE;
+    static_assert(NPRE >= 0 && NPRE <= DB, "prefetch within the first key chunk");
+    auto read_v = [&](const uint8_t *vbuf, int kc, int db) {
+        const uint8_t *vp = vbuf + v_rd[db] + kc * 16 * ROWB;
+        const uint2 lo = ds_read_tr(vp);
+        const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
+        return u32x4{lo.x, lo.y, hi4.x, hi4.y};
+    };
+    u32x4 vpre[NPRE > 0 ? NPRE : 1];
     auto mfma_phase = [&](const LoadPlan &pl, const uint8_t *vbuf, const uint8_t *kbuf) {
+        if (PP_PRIO) __builtin_amdgcn_s_setprio(PP_PRIO);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const uint8_t *vp = vbuf + v_rd[db] + kc * 16 * ROWB;
-                const uint2 lo = ds_read_tr(vp);
-                const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
-                oacc[db] = Ops::mma(u32x4{lo.x, lo.y, hi4.x, hi4.y}, pk[kc], oacc[db]);
+                const u32x4 a = (kc == 0 && db < NPRE) ? vpre[db] : read_v(vbuf, kc, db);
+                oacc[db] = Ops::mma(a, pk[kc], oacc[db]);
                 if (kc == 1 && db == 0) issue(pl, 0);
             }
 #pragma unroll
@@ -1036,9 +1050,10 @@ void fa_fwd_mfma_pp_kernel(Params p)
             }
         constexpr int LEAD = PP_LEAD;
         constexpr int NM = NPV + NQK;
-        static_assert(LEAD >= 1 && LEAD <= NPV, "read lead");
-        // MFMA n (n < NPV: PV, else QK) is preceded by the reads of MFMA n + LEAD
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
+        static_assert(LEAD >= NPRE && LEAD <= NPV, "read lead");
+        // MFMA n (n < NPV: PV, else QK) is preceded by the reads of MFMA
+        // n + LEAD; MFMAs below NPRE need none
+        if constexpr (LEAD > NPRE) __builtin_amdgcn_sched_group_barrier(0x100, 2 * (LEAD - NPRE), 0);
 #pragma unroll
         for (int n = 0; n < NPV - LEAD; ++n) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -1050,13 +1065,16 @@ void fa_fwd_mfma_pp_kernel(Params p)
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
+        if (PP_PRIO) __builtin_amdgcn_s_setprio(0);
         // S must exist before the barrier
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) __asm__ volatile("" : "+v"(st[kb]));
     };
     // Online softmax of tile j in slot t (vector ALU only): mask, row max,
     // lazy rescale, p = exp2(s*c - m*c) rounded to the I/O type, row sum.
-    auto softmax = [&](const LoadPlan &pl, int j) {
+    auto softmax = [&](const LoadPlan &pl, int j, const uint8_t *vnext) {
+#pragma unroll
+        for (int db = 0; db < NPRE; ++db) vpre[db] = read_v(vnext, 0, db);
         issue(pl, 0);
         const int k0 = j * BN;
         if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
@@ -1108,39 +1126,39 @@ void fa_fwd_mfma_pp_kernel(Params p)
         for (int kc = 0; kc < KC; ++kc) __asm__ volatile("" : "+v"(pk[kc]));
     };
     static_assert(LOADS <= 2, "two load points per phase");
-    // End of slot t: odd slots first wait for all but this slot's loads
-    // (so K_{s+1} and V_s have landed), then every slot ends in a barrier.
+    // End of slot t: wait for all loads but this slot's, then a barrier.
     // Group 1 ends on an MFMA phase in slot 2*ntiles + 1, after which no
     // barrier is needed.
     const int last_slot = 2 * ntiles + 1;
     auto slot_end = [&](int t) {
-        if (t & 1) wait_vmcnt<LOADS>();
+        wait_vmcnt<LOADS>();
         if (t != last_slot) __syncthreads();
     };
 
-    // Loads per slot: group 0 runs SM_j in slot 2j+1 (loads V_{j+1}) and
-    // PV_j+QK_{j+1} in slot 2j+2 (loads K_{j+2}); group 1 runs SM_j in slot
-    // 2j+2 (K_{j+2}) and PV_j+QK_{j+1} in slot 2j+3 (V_{j+2}).
+    // Loads per slot: group 0 runs SM_j in slot 2j+1 (loads K_{j+2}) and
+    // PV_j+QK_{j+1} in slot 2j+2 (loads V_{j+2}); group 1 runs SM_j in slot
+    // 2j+2 (V_{j+2}) and PV_j+QK_{j+1} in slot 2j+3 (K_{j+3}).
     {
-        const LoadPlan k0p = plan(true, 0), v0p = plan(false, 0);
+        const LoadPlan k0p = plan(true, 0), v0p = plan(false, 0), k1p = plan(true, 1);
 #pragma unroll
         for (int r = 0; r < LOADS; ++r) {
             issue(k0p, r);
             issue(v0p, r);
+            issue(k1p, r);
         }
     }
     wait_vmcnt<0>();
     __syncthreads();
     int t = 0;
-    if (grp == 1) {   // group 1 starts one slot late, loading its share of K_1
-        const LoadPlan pl = plan(true, 1);
+    if (grp == 1) {   // group 1 starts one slot late, loading its share of V_1
+        const LoadPlan pl = plan(false, 1);
 #pragma unroll
         for (int r = 0; r < LOADS; ++r) issue(pl, r);
         slot_end(t);
         ++t;
     }
-    {   // S^T of tile 0 (loads K_1 in group 0's slot 0, V_1 in group 1's slot 1)
-        const LoadPlan pl = plan(grp == 0, 1);
+    {   // S^T of tile 0 (loads V_1 in group 0's slot 0, K_2 in group 1's slot 1)
+        const LoadPlan pl = plan(grp == 1, 1 + grp);
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
@@ -1152,29 +1170,27 @@ void fa_fwd_mfma_pp_kernel(Params p)
         slot_end(t);
         ++t;
     }
-    // unrolled by four so that every LDS read address is a constant offset
+    // unrolled by three so that every LDS read address is a constant offset
     auto tile = [&](int j, const uint8_t *vbuf, const uint8_t *kbuf) {
         {
-            const LoadPlan pl = plan(grp == 1, j + 1 + grp);
-            softmax(pl, j);
+            const LoadPlan pl = plan(grp == 0, j + 2);
+            softmax(pl, j, vbuf);
             slot_end(t);
             ++t;
         }
         {
-            const LoadPlan pl = plan(grp == 0, j + 2);
+            const LoadPlan pl = plan(grp == 1, j + 2 + grp);
             mfma_phase(pl, vbuf, kbuf);
             slot_end(t);
             ++t;
         }
     };
-    for (int j = 0; j < ntiles; j += 4) {
+    for (int j = 0; j < ntiles; j += 3) {
         tile(j, v_lds[0], k_lds[1]);
         if (j + 1 >= ntiles) break;
-        tile(j + 1, v_lds[1], k_lds[0]);
+        tile(j + 1, v_lds[1], k_lds[2]);
         if (j + 2 >= ntiles) break;
-        tile(j + 2, v_lds[2], k_lds[1]);
-        if (j + 3 >= ntiles) break;
-        tile(j + 3, v_lds[3], k_lds[0]);
+        tile(j + 2, v_lds[2], k_lds[0]);
     }
     // no load may still be writing LDS when the workgroup ends
     wait_vmcnt<0>();

@@ -128,6 +128,18 @@ def test_tile_variants(tile, D, dt, monkeypatch):
         check_full(q, k, v, causal, 0.11, dt, f"tile={tile}")
 
 
+# The ping-pong kernel unrolls its tile loop and pairs wave groups slot by
+# slot: cover every way the loop can end (1..5 key tiles, ragged and exact)
+# and query blocks shorter than one workgroup.
+@pytest.mark.parametrize("Lk", [1, 63, 64, 65, 128, 129, 192, 193, 256, 257, 320])
+def test_pingpong_tile_counts(Lk, monkeypatch):
+    monkeypatch.setenv("FA_TILE", "8x1x64x2x3")
+    for D, dt in ((128, "bf16"), (64, "f16")):
+        for Lq, causal in ((1, False), (257, False), (300, True)):
+            q, k, v = inputs.make_qkv(1, 2, Lq, Lk, D, dt, seed=Lk * 7 + Lq + D)
+            check_full(q, k, v, causal, 0.09, dt, f"pingpong Lk={Lk}")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5, 1e-3])
 def test_scale_values(scale):
     q, k, v = inputs.make_qkv(1, 2, 150, 200, 64, "bf16", seed=11)
