@@ -22,10 +22,11 @@ struct FwdArgs {
 // Tile shape of the MFMA kernel: NW waves per workgroup, each wave owning
 // QB blocks of 32 queries (so BM = NW * QB * 32 query rows per workgroup),
 // BN keys per K/V tile, OCC waves per SIMD the register budget is cut for,
-// and the K/V staging pipe (0: through VGPRs with a transposing V store and
-// one tile per step; 2: direct global-to-LDS loads, transposed V reads, and
-// the QK^T of the next tile software-pipelined under the softmax of this
-// one).
+// and the K/V pipe: 0 stages tiles through VGPRs with a transposing V store,
+// one tile per step; 2 loads tiles straight into LDS, reads V^T with
+// transposing LDS reads and software-pipelines the QK^T of the next tile
+// under the softmax of this one; 3 (8x1x64x2 only) is the ping-pong kernel,
+// in which the two waves of each SIMD alternate MFMA and softmax phases.
 struct MfmaTile {
     int nw, qb, bn, occ, pipe;
 };

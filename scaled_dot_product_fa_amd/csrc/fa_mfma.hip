@@ -1337,12 +1337,14 @@ bool mfma_supported(const FwdArgs &a)
 
 MfmaTile mfma_choose_tile(const FwdArgs &a)
 {
-    // Direct loads with the software-pipelined step.  8 waves (256 query
-    // rows) per workgroup when that still gives at least two workgroups per
-    // CU (512 for 256 CUs); otherwise 4 waves (128 rows) for more
-    // workgroups.
+    // 8 waves (256 query rows) per workgroup when that still gives at least
+    // two workgroups per CU (512 for 256 CUs); otherwise 4 waves (128 rows)
+    // with the software-pipelined step, for more workgroups.  With 8 waves,
+    // D = 128 uses the ping-pong kernel, whose MFMA phase (32 MFMAs) is about
+    // as long as the softmax phase it pairs with; at D = 64 the MFMA phase
+    // is half that and the software-pipelined step is as fast.
     const int64_t wgs256 = a.B * a.H * ((a.Lq + 255) / 256);
-    if (wgs256 >= 512) return MfmaTile{8, 1, 64, 2, 2};
+    if (wgs256 >= 512) return MfmaTile{8, 1, 64, 2, a.D == 128 ? 3 : 2};
     return MfmaTile{4, 1, 64, 2, 2};
 }
 
