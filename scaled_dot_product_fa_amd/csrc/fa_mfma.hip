@@ -861,7 +861,7 @@ void fa_fwd_mfma_dma_kernel(Params p)
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong variant (8 waves, 32 query rows each, 64-key tiles).  The two
+// Ping-pong variant (8 waves, 32 query rows each, BN-key tiles).  The two
 // waves that share a SIMD (w and w + 4) run half a step apart: while one
 // issues the MFMAs of its step (P_j V_j for tile j and S_{j+1} = Q K_{j+1}^T
 // for the next tile, reading K and V from LDS), the other runs the softmax
@@ -879,11 +879,11 @@ void fa_fwd_mfma_dma_kernel(Params p)
 // phase reads are visible one slot early and the softmax phase before it
 // prefetches the phase's first V operands into registers.
 // ---------------------------------------------------------------------------
-template <typename Ops, int D, bool CAUSAL>
+template <typename Ops, int D, bool CAUSAL, int BN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_mfma_pp_kernel(Params p)
 {
-    constexpr int NW = 8, BN = 64;
+    constexpr int NW = 8;
     constexpr int BM = NW * 32;          // query rows per workgroup
     constexpr int DC = D / 16;           // 16-dim chunks (k of the QK^T MFMA)
     constexpr int DB = D / 32;           // 32-dim blocks (rows of O^T)
@@ -894,6 +894,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
     constexpr int TILEB = BN * ROWB;     // bytes of one K (or V) tile
     constexpr int LOADS = TILEB / (NW * 64 * 16);   // loads per wave per tile
     static_assert(LOADS >= 1 && TILEB % (NW * 64 * 16) == 0, "tile split");
+    static_assert(6 * TILEB <= 160 * 1024, "three K and three V buffers fit the LDS");
 
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds[3][TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds[3][TILEB];
@@ -1031,6 +1032,8 @@ void fa_fwd_mfma_pp_kernel(Params p)
         return u32x4{lo.x, lo.y, hi4.x, hi4.y};
     };
     u32x4 vpre[NPRE > 0 ? NPRE : 1];
+    // the MFMA (PV first, then QK^T) after which load piece r is issued
+    auto load_at = [](int r) { return 2 + r * ((NPV + NQK) / LOADS); };
     auto mfma_phase = [&](const LoadPlan &pl, const uint8_t *vbuf, const uint8_t *kbuf) {
         if (PP_PRIO) __builtin_amdgcn_s_setprio(PP_PRIO);
 #pragma unroll
@@ -1039,14 +1042,18 @@ void fa_fwd_mfma_pp_kernel(Params p)
             for (int db = 0; db < DB; ++db) {
                 const u32x4 a = (kc == 0 && db < NPRE) ? vpre[db] : read_v(vbuf, kc, db);
                 oacc[db] = Ops::mma(a, pk[kc], oacc[db]);
-                if (kc == 1 && db == 0) issue(pl, 0);
+#pragma unroll
+                for (int r = 0; r < LOADS; ++r)
+                    if (kc * DB + db == load_at(r)) issue(pl, r);
             }
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 qk_mma(kbuf, dc, kb);
-                if (LOADS > 1 && dc == 1 && kb == 0) issue(pl, LOADS - 1);
+#pragma unroll
+                for (int r = 0; r < LOADS; ++r)
+                    if (NPV + dc * KB + kb == load_at(r)) issue(pl, r);
             }
         constexpr int LEAD = PP_LEAD;
         constexpr int NM = NPV + NQK;
@@ -1075,7 +1082,6 @@ void fa_fwd_mfma_pp_kernel(Params p)
     auto softmax = [&](const LoadPlan &pl, int j, const uint8_t *vnext) {
 #pragma unroll
         for (int db = 0; db < NPRE; ++db) vpre[db] = read_v(vnext, 0, db);
-        issue(pl, 0);
         const int k0 = j * BN;
         if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
 #pragma unroll
@@ -1109,7 +1115,9 @@ void fa_fwd_mfma_pp_kernel(Params p)
         float r4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            if (LOADS > 1 && kc == KC / 2) issue(pl, LOADS - 1);
+#pragma unroll
+            for (int r = 0; r < LOADS; ++r)
+                if (kc == r * KC / LOADS) issue(pl, r);
             const int kb = kc >> 1, h = kc & 1;
             float e[8];
 #pragma unroll
@@ -1125,7 +1133,6 @@ void fa_fwd_mfma_pp_kernel(Params p)
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) __asm__ volatile("" : "+v"(pk[kc]));
     };
-    static_assert(LOADS <= 2, "two load points per phase");
     // End of slot t: wait for all loads but this slot's, then a barrier.
     // Group 1 ends on an MFMA phase in slot 2*ntiles + 1, after which no
     // barrier is needed.
@@ -1214,7 +1221,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
     }
 }
 
-template <typename Ops, int D, bool CAUSAL>
+template <typename Ops, int D, bool CAUSAL, int BN>
 hipError_t launch_pp(const FwdArgs &a)
 {
     constexpr int BM = 256;
@@ -1231,7 +1238,7 @@ hipError_t launch_pp(const FwdArgs &a)
     p.scale = a.scale;
     p.c = a.scale * kLog2e;
     const int64_t nwg = (int64_t)p.BH * p.ntq;
-    hipLaunchKernelGGL((fa_fwd_mfma_pp_kernel<Ops, D, CAUSAL>), dim3((unsigned)nwg), dim3(512),
+    hipLaunchKernelGGL((fa_fwd_mfma_pp_kernel<Ops, D, CAUSAL, BN>), dim3((unsigned)nwg), dim3(512),
                        0, a.stream, p);
     return hipGetLastError();
 }
@@ -1310,11 +1317,18 @@ template <typename Ops>
 hipError_t launch_ops(const FwdArgs &a, const MfmaTile &t)
 {
     if (t.pipe == 3) {
-        if (!(t.nw == 8 && t.qb == 1 && t.bn == 64 && t.occ == 2))
+        // 8 waves; 64-key tiles, or 128-key tiles at D = 64 (six buffers of
+        // 32 KB would not fit the LDS at D = 128)
+        if (!(t.nw == 8 && t.qb == 1 && t.occ == 2)) return hipErrorInvalidConfiguration;
+        if (a.D == 64) {
+            if (t.bn == 128)
+                return a.causal ? launch_pp<Ops, 64, true, 128>(a) : launch_pp<Ops, 64, false, 128>(a);
+            if (t.bn == 64)
+                return a.causal ? launch_pp<Ops, 64, true, 64>(a) : launch_pp<Ops, 64, false, 64>(a);
             return hipErrorInvalidConfiguration;
-        if (a.D == 64)
-            return a.causal ? launch_pp<Ops, 64, true>(a) : launch_pp<Ops, 64, false>(a);
-        return a.causal ? launch_pp<Ops, 128, true>(a) : launch_pp<Ops, 128, false>(a);
+        }
+        if (t.bn != 64) return hipErrorInvalidConfiguration;
+        return a.causal ? launch_pp<Ops, 128, true, 64>(a) : launch_pp<Ops, 128, false, 64>(a);
     }
     if (t.pipe == 2) {
         if (a.D == 64)
@@ -1338,13 +1352,13 @@ bool mfma_supported(const FwdArgs &a)
 MfmaTile mfma_choose_tile(const FwdArgs &a)
 {
     // 8 waves (256 query rows) per workgroup when that still gives at least
-    // two workgroups per CU (512 for 256 CUs); otherwise 4 waves (128 rows)
-    // with the software-pipelined step, for more workgroups.  With 8 waves,
-    // D = 128 uses the ping-pong kernel, whose MFMA phase (32 MFMAs) is about
-    // as long as the softmax phase it pairs with; at D = 64 the MFMA phase
-    // is half that and the software-pipelined step is as fast.
+    // two workgroups per CU (512 for 256 CUs): the ping-pong kernel, with
+    // 64-key tiles at D = 128 (32 MFMAs per phase) and 128-key tiles at
+    // D = 64 (also 32 MFMAs per phase, and half as many barriers per key).
+    // Otherwise 4 waves (128 rows) with the software-pipelined step, for
+    // more workgroups.
     const int64_t wgs256 = a.B * a.H * ((a.Lq + 255) / 256);
-    if (wgs256 >= 512) return MfmaTile{8, 1, 64, 2, a.D == 128 ? 3 : 2};
+    if (wgs256 >= 512) return MfmaTile{8, 1, a.D == 128 ? 64 : 128, 2, 3};
     return MfmaTile{4, 1, 64, 2, 2};
 }
 
