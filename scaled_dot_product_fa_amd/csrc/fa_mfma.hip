@@ -60,9 +60,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #ifndef PP_LEAD
 #define PP_LEAD 4
 #endif
-#ifndef PP_PRE
-#define PP_PRE 2
-#endif
 #ifndef PP_PRIO
 #define PP_PRIO 1
 #endif
@@ -875,9 +872,11 @@ void fa_fwd_mfma_dma_kernel(Params p)
 // Every slot loads one tile, in pieces spread through both phases so that
 // no wave stalls behind a burst of loads: slot 2s loads V_{s+1} and slot
 // 2s+1 loads K_{s+2}, three LDS buffers each.  Before each barrier a wave
-// waits for its loads of all earlier slots (vmcnt), so the tiles an MFMA
-// phase reads are visible one slot early and the softmax phase before it
-// prefetches the phase's first V operands into registers.
+// waits for its loads of all earlier slots (vmcnt), so every load has more
+// than a slot to land.  (Reading the first V operands of an MFMA phase
+// already in the softmax phase before it, which the early visibility
+// allows, measured slower: those reads compete with the partner's MFMA
+// phase.)
 // ---------------------------------------------------------------------------
 template <typename Ops, int D, bool CAUSAL, int BN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1016,22 +1015,17 @@ void fa_fwd_mfma_pp_kernel(Params p)
     };
     // One MFMA phase: O^T += V^T P^T for tile j (A = 32 dims x 16 keys of V
     // from two transposed LDS reads, B = P^T), then S^T = K Q^T for tile j+1.
-    // The first NPRE V operands were read during the softmax phase before.
     // The last tile's phase also runs the QK^T half, on whatever the K
     // buffer holds (the result is never used), so that every phase is one
-    // straight-line block.  The other LDS reads are pinned PP_LEAD MFMAs
-    // ahead of their use; the slot's loads go out after the first PV MFMAs
-    // and the first QK^T MFMAs.
+    // straight-line block.  The LDS reads are pinned PP_LEAD MFMAs ahead of
+    // their use; the slot's loads are spread over the phase.
     constexpr int NPV = KC * DB, NQK = DC * KB;
-    constexpr int NPRE = PP_PRE;
-    static_assert(NPRE >= 0 && NPRE <= DB, "prefetch within the first key chunk");
     auto read_v = [&](const uint8_t *vbuf, int kc, int db) {
         const uint8_t *vp = vbuf + v_rd[db] + kc * 16 * ROWB;
         const uint2 lo = ds_read_tr(vp);
         const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
         return u32x4{lo.x, lo.y, hi4.x, hi4.y};
     };
-    u32x4 vpre[NPRE > 0 ? NPRE : 1];
     // the MFMA (PV first, then QK^T) after which load piece r is issued
     auto load_at = [](int r) { return 2 + r * ((NPV + NQK) / LOADS); };
     auto mfma_phase = [&](const LoadPlan &pl, const uint8_t *vbuf, const uint8_t *kbuf) {
@@ -1040,7 +1034,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const u32x4 a = (kc == 0 && db < NPRE) ? vpre[db] : read_v(vbuf, kc, db);
+                const u32x4 a = read_v(vbuf, kc, db);
                 oacc[db] = Ops::mma(a, pk[kc], oacc[db]);
 #pragma unroll
                 for (int r = 0; r < LOADS; ++r)
@@ -1057,10 +1051,10 @@ void fa_fwd_mfma_pp_kernel(Params p)
             }
         constexpr int LEAD = PP_LEAD;
         constexpr int NM = NPV + NQK;
-        static_assert(LEAD >= NPRE && LEAD <= NPV, "read lead");
+        static_assert(LEAD >= 1 && LEAD <= NPV, "read lead");
         // MFMA n (n < NPV: PV, else QK) is preceded by the reads of MFMA
-        // n + LEAD; MFMAs below NPRE need none
-        if constexpr (LEAD > NPRE) __builtin_amdgcn_sched_group_barrier(0x100, 2 * (LEAD - NPRE), 0);
+        // n + LEAD
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
 #pragma unroll
         for (int n = 0; n < NPV - LEAD; ++n) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -1079,9 +1073,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
     };
     // Online softmax of tile j in slot t (vector ALU only): mask, row max,
     // lazy rescale, p = exp2(s*c - m*c) rounded to the I/O type, row sum.
-    auto softmax = [&](const LoadPlan &pl, int j, const uint8_t *vnext) {
-#pragma unroll
-        for (int db = 0; db < NPRE; ++db) vpre[db] = read_v(vnext, 0, db);
+    auto softmax = [&](const LoadPlan &pl, int j) {
         const int k0 = j * BN;
         if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
 #pragma unroll
@@ -1181,7 +1173,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
     auto tile = [&](int j, const uint8_t *vbuf, const uint8_t *kbuf) {
         {
             const LoadPlan pl = plan(grp == 0, j + 2);
-            softmax(pl, j, vbuf);
+            softmax(pl, j);
             slot_end(t);
             ++t;
         }
