@@ -1343,14 +1343,27 @@ bool mfma_supported(const FwdArgs &a)
 
 MfmaTile mfma_choose_tile(const FwdArgs &a)
 {
-    // 8 waves (256 query rows) per workgroup when that still gives at least
-    // two workgroups per CU (512 for 256 CUs): the ping-pong kernel, with
-    // 64-key tiles at D = 128 (32 MFMAs per phase) and 128-key tiles at
-    // D = 64 (also 32 MFMAs per phase, and half as many barriers per key).
-    // Otherwise 4 waves (128 rows) with the software-pipelined step, for
-    // more workgroups.
-    const int64_t wgs256 = a.B * a.H * ((a.Lq + 255) / 256);
-    if (wgs256 >= 512) return MfmaTile{8, 1, a.D == 128 ? 64 : 128, 2, 3};
+    // Static table from an offline sweep of every tile over shape classes
+    // (scaled_dot_product_fa_amd/tune.py, timings in tiles.json).  In short:
+    // the ping-pong kernel (8 waves, 256 query rows; 64-key tiles at
+    // D = 128, 128-key tiles at D = 64) once there are 512+ blocks of 256
+    // rows and 2048+ visible keys per row; otherwise 4 waves of the
+    // software-pipelined kernel (128 rows per workgroup, twice as many
+    // workgroups).
+    struct TileRule {
+        int d, causal;
+        int64_t min_blocks, min_kv;
+        MfmaTile tile;
+    };
+    static const TileRule kRules[] = {
+#include "fa_tiles.inc"
+    };
+    const int64_t blocks = a.B * a.H * ((a.Lq + 255) / 256);
+    const int64_t kv = a.causal ? (a.Lk < a.Lq ? a.Lk : a.Lq) : a.Lk;
+    for (const TileRule &r : kRules)
+        if (r.d == a.D && r.causal == (a.causal ? 1 : 0) && blocks >= r.min_blocks &&
+            kv >= r.min_kv)
+            return r.tile;
     return MfmaTile{4, 1, 64, 2, 2};
 }
 
