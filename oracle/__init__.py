@@ -54,6 +54,9 @@ def _bind(lib):
     lib.oracle_probs.argtypes = [_F64P, _F64P, _F64P, _I64, _I64, _I64, _I64,
                                  _I64, ctypes.c_int, ctypes.c_double]
     lib.oracle_probs.restype = ctypes.c_int
+    lib.oracle_attention_bwd.argtypes = [_F64P] * 8 + [_I64] * 5 + [
+        ctypes.c_int, ctypes.c_double]
+    lib.oracle_attention_bwd.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -143,6 +146,32 @@ def probs(q, k, causal: bool = False, scale: float | None = None, lib=None):
     if rc != 0:
         raise RuntimeError(f"oracle_probs failed ({rc})")
     return p
+
+
+def attention_bwd(q, k, v, dout, causal: bool = False,
+                  scale: float | None = None, lib=None, with_delta=False):
+    """fp64 gradients (dq, dk, dv) of the forward for an incoming gradient
+    ``dout`` of o (lse takes no gradient).  The plain chain rule through the
+    forward definition; the C source states each step.  With ``with_delta``
+    also returns delta [B,H,Lq], delta_i = sum_j p_ij (dout_i . v_j)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, Lq, Lk, D = _shapes(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have the shape of q")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    delta = np.empty((B, H, Lq), dtype=np.float64)
+    rc = (lib or load()).oracle_attention_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(delta), B, H, Lq, Lk, D, int(bool(causal)), float(scale))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_bwd failed ({rc})")
+    if with_delta:
+        return dq, dk, dv, delta
+    return dq, dk, dv
 
 
 def num_threads(lib=None) -> int:

@@ -212,6 +212,94 @@ int oracle_probs(const double *q, const double *k, double *p_out, int64_t B,
     return 0;
 }
 
+/*
+ * Gradients of the forward above with respect to q, k and v, for an incoming
+ * gradient dout of o.  The pages implement only the forward: the
+ * FlashAttention-2 article's host wrapper keeps q, k, v, o and the row
+ * statistic for a backward pass, and its closing remarks leave the backward
+ * as future work; the same article's account of the IO-aware idea notes
+ * that a backward pass may recompute the probabilities rather than store
+ * them.  The backward is therefore the plain chain rule through the
+ * definition in this file's header, with lse an auxiliary output that takes
+ * no gradient.  Per (b, h), with p the probabilities of the forward:
+ *
+ *   dv_j  = sum_i p_ij dout_i
+ *   dp_ij = dout_i . v_j
+ *   delta_i = sum_j p_ij dp_ij
+ *   ds_ij = p_ij (dp_ij - delta_i)          (softmax Jacobian; 0 if masked)
+ *   dq_i  = scale * sum_j ds_ij k_j
+ *   dk_j  = scale * sum_i ds_ij q_i
+ *
+ * Layouts as for oracle_attention; dout and dq are [B,H,Lq,D], dk and dv
+ * [B,H,Lk,D]; delta [B,H,Lq] receives delta_i (may be NULL).  Each head keeps p and ds as dense [Lq, Lk] fp64 matrices.
+ * Rows are done in parallel (p, ds, dq), then keys (dk, dv), so no sum is
+ * shared between threads.  Returns 0, or -1 on a bad shape or allocation
+ * failure.
+ */
+int oracle_attention_bwd(const double *q, const double *k, const double *v,
+                         const double *dout, double *dq, double *dk,
+                         double *dv, double *delta_out, int64_t B, int64_t H,
+                         int64_t Lq,
+                         int64_t Lk, int64_t D, int causal, double scale)
+{
+    int64_t bh;
+    double *p, *ds;
+    if (!check_shape(B, H, Lq, Lk, D)) return -1;
+    p = (double *)malloc(sizeof(double) * (size_t)(Lq * Lk > 0 ? Lq * Lk : 1));
+    ds = (double *)malloc(sizeof(double) * (size_t)(Lq * Lk > 0 ? Lq * Lk : 1));
+    if (!p || !ds) {
+        free(p);
+        free(ds);
+        return -1;
+    }
+    for (bh = 0; bh < B * H; ++bh) {
+        const double *qh = q + bh * Lq * D, *kh = k + bh * Lk * D;
+        const double *vh = v + bh * Lk * D, *gh = dout + bh * Lq * D;
+        double *dqh = dq + bh * Lq * D, *dkh = dk + bh * Lk * D;
+        double *dvh = dv + bh * Lk * D;
+        int64_t i, j;
+#pragma omp parallel for schedule(dynamic, 8)
+        for (i = 0; i < Lq; ++i) {
+            double *pi = p + i * Lk, *dsi = ds + i * Lk;
+            const double *gi = gh + i * D;
+            int64_t jend = visible_end(i, Lk, causal), jj, d;
+            double m, l, delta = 0.0;
+            softmax_row(qh + i * D, kh, Lk, D, jend, scale, pi, &m, &l);
+            for (jj = 0; jj < Lk; ++jj) dsi[jj] = 0.0;
+            for (jj = 0; jj < jend; ++jj) {
+                const double *vj = vh + jj * D;
+                double dp = 0.0;
+                for (d = 0; d < D; ++d) dp += gi[d] * vj[d];
+                dsi[jj] = dp;
+                delta += pi[jj] * dp;
+            }
+            for (jj = 0; jj < jend; ++jj) dsi[jj] = pi[jj] * (dsi[jj] - delta);
+            if (delta_out) delta_out[bh * Lq + i] = delta;
+            for (d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (jj = 0; jj < jend; ++jj) acc += dsi[jj] * kh[jj * D + d];
+                dqh[i * D + d] = scale * acc;
+            }
+        }
+#pragma omp parallel for schedule(dynamic, 8)
+        for (j = 0; j < Lk; ++j) {
+            int64_t ii, d;
+            for (d = 0; d < D; ++d) {
+                double accv = 0.0, acck = 0.0;
+                for (ii = 0; ii < Lq; ++ii) {
+                    accv += p[ii * Lk + j] * gh[ii * D + d];
+                    acck += ds[ii * Lk + j] * qh[ii * D + d];
+                }
+                dvh[j * D + d] = accv;
+                dkh[j * D + d] = scale * acck;
+            }
+        }
+    }
+    free(p);
+    free(ds);
+    return 0;
+}
+
 /* Threads the OpenMP runtime will use for the calls above. */
 int oracle_num_threads(void)
 {
