@@ -36,13 +36,13 @@ enum fa_dtype {
 /* Return codes.  FA_OK is zero; every error is positive. */
 enum fa_status {
     FA_OK = 0,
-    FA_ERR_NULL = 1,      /* q, k, v or o is NULL */
+    FA_ERR_NULL = 1,      /* a required pointer is NULL */
     FA_ERR_SHAPE = 2,     /* B, H, Lq or Lk < 1, or a size past the limits */
     FA_ERR_HEAD_DIM = 3,  /* D is not 64 or 128 */
     FA_ERR_DTYPE = 4,     /* dtype is not one of enum fa_dtype */
     FA_ERR_SCALE = 5,     /* scale is NaN or infinite */
-    FA_ERR_ALIGN = 6,     /* q, k, v, o not 16-byte aligned, lse not 4-byte */
-    FA_ERR_ALIAS = 7,     /* o or lse overlaps an input, or o overlaps lse */
+    FA_ERR_ALIGN = 6,     /* a tensor not 16-byte aligned, lse/delta not 4-byte */
+    FA_ERR_ALIAS = 7,     /* an output overlaps an input or another output */
     FA_ERR_POINTER = 8,   /* a pointer is not device memory of this device */
     FA_ERR_LAUNCH = 9     /* the HIP runtime rejected the kernel launch */
 };
@@ -91,6 +91,55 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
            int causal, float scale, int dtype, void *stream);
 
+/*
+ * fa_bwd -- gradients of the attention forward on one GPU, enqueued on
+ * `stream`.
+ *
+ * The pages implement only the forward.  The FlashAttention-2 forward
+ * article's host wrapper keeps Q, K, V, O and the row statistic for a
+ * backward pass, its account of the IO-aware idea notes that a backward may
+ * recompute the probabilities rather than store them, and its closing
+ * remarks leave the backward as future work.  This entry point is the chain
+ * rule through the forward's definition (see fa_fwd), with the probabilities
+ * recomputed from lse; lse itself takes no gradient.  For each (b, h):
+ *
+ *   p_ij    = exp(s_ij - lse_i)   (s_ij as in fa_fwd; 0 for invisible keys)
+ *   delta_i = dout_i . o_i
+ *   ds_ij   = p_ij (dout_i . v_j - delta_i)
+ *   dv_j    = sum_i p_ij dout_i
+ *   dk_j    = scale * sum_i ds_ij q_i
+ *   dq_i    = scale * sum_j ds_ij k_j
+ *
+ * q, k, v, causal, scale, dtype, B, H, Lq, Lk, D: exactly as passed to the
+ *              fa_fwd call that produced o and lse.
+ * o    [B, H, Lq, D]  device pointer, the forward output (I/O type).
+ * lse  [B, H, Lq]     device pointer to fp32, the forward's row statistic.
+ * dout [B, H, Lq, D]  device pointer, the incoming gradient of o.
+ * dq   [B, H, Lq, D]  device pointer, written (I/O type).
+ * dk   [B, H, Lk, D]  device pointer, written (I/O type).
+ * dv   [B, H, Lk, D]  device pointer, written (I/O type).
+ * delta [B, H, Lq]    device pointer to fp32 owned by the caller, written
+ *              with delta_i (the library allocates nothing, so this per-row
+ *              workspace is an argument; its contents are valid after the
+ *              call completes).
+ * All tensors contiguous row-major (D fastest), same element type.
+ *
+ * bf16/fp16 inputs: products exact, sums in fp32, probabilities and ds
+ * rounded to the I/O type before they multiply tensors, gradients rounded to
+ * nearest-even into the I/O type.  fp32 inputs: fp32 throughout.
+ *
+ * Ownership and errors as for fa_fwd: every check runs on the host before
+ * anything is enqueued (FA_ERR_NULL for any NULL pointer, FA_ERR_ALIGN when a
+ * tensor is not 16-byte or lse/delta not 4-byte aligned, FA_ERR_ALIAS when
+ * dq, dk, dv or delta overlaps an input or another output); nothing is
+ * written on an error.  Several kernels are enqueued in order on `stream`.
+ * Deterministic: no atomics, the same inputs give the same bits.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+           const float *lse, const void *dout, void *dq, void *dk, void *dv,
+           float *delta, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+           int64_t D, int causal, float scale, int dtype, void *stream);
+
 /* Static text for a status code ("unknown status" for anything else). */
 const char *fa_status_string(int status);
 
@@ -102,6 +151,14 @@ const char *fa_status_string(int status);
  */
 const char *fa_kernel_name(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                            int64_t D, int causal, float scale, int dtype);
+
+/*
+ * fa_bwd_kernel_name -- name of the gradient kernel (dk/dv) fa_bwd would
+ * launch for these arguments, or NULL when fa_bwd would reject them.  Pure
+ * host logic, like fa_kernel_name.
+ */
+const char *fa_bwd_kernel_name(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                               int64_t D, int causal, float scale, int dtype);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int fa_version(void);

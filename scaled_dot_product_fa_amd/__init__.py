@@ -1,19 +1,21 @@
-"""MI355X (gfx950) FlashAttention-2 forward.
+"""MI355X (gfx950) FlashAttention-2 forward, and its backward.
 
 ``forward(q, k, v, causal=False, scale=None)`` returns ``(o, lse)`` for
 contiguous ``[B, H, L, D]`` device tensors (bf16, fp16 or fp32; D = 64 or
-128).  PyTorch provides the device memory and the stream; the computation is
+128); ``backward(q, k, v, o, lse, dout, ...)`` returns ``(dq, dk, dv)``.  PyTorch provides the device memory and the stream; the computation is
 the HIP kernels in ``libfa.so`` behind the C ABI of ``include/fa.h``.
 """
 from __future__ import annotations
 
 import math
 
-from ._lib import (FA_BF16, FA_F16, FA_F32, FaError, fa_fwd, fa_kernel_name,
+from ._lib import (FA_BF16, FA_F16, FA_F32, FaError, fa_bwd,
+                   fa_bwd_kernel_name, fa_fwd, fa_kernel_name,
                    fa_status_string, fa_version, load)
 
-__all__ = ["forward", "fa_fwd", "fa_kernel_name", "fa_status_string",
-           "fa_version", "FaError", "dtype_code", "load"]
+__all__ = ["forward", "backward", "fa_fwd", "fa_bwd", "fa_kernel_name",
+           "fa_bwd_kernel_name", "fa_status_string", "fa_version", "FaError",
+           "dtype_code", "load"]
 
 
 def dtype_code(dtype) -> int:
@@ -65,3 +67,52 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None,
     if rc != 0:
         raise FaError(rc, fa_status_string(rc))
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False,
+             scale: float | None = None, dq=None, dk=None, dv=None,
+             delta=None, stream=None):
+    """Gradients (dq, dk, dv) of the forward for an incoming ``dout``.
+
+    q, k, v, causal and scale as given to :func:`forward`; o and lse are what
+    it returned; dout is like o.  ``dq``/``dk``/``dv`` and the fp32 [B,H,Lq]
+    workspace ``delta`` may be preallocated.  Raises FaError on a status
+    other than FA_OK.
+    """
+    import torch
+    load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, L, D]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, o, dout must share one dtype")
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    if (tuple(k.shape) != (B, H, Lk, D) or tuple(v.shape) != (B, H, Lk, D)
+            or tuple(o.shape) != (B, H, Lq, D)
+            or tuple(dout.shape) != (B, H, Lq, D)):
+        raise ValueError("shapes must be q/o/dout [B,H,Lq,D], k/v [B,H,Lk,D]")
+    if (lse is None or not lse.is_cuda or lse.dtype != torch.float32
+            or tuple(lse.shape) != (B, H, Lq) or not lse.is_contiguous()):
+        raise ValueError("lse must be the forward's fp32 [B, H, Lq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                dv.data_ptr(), delta.data_ptr(), B, H, Lq, Lk, D,
+                int(bool(causal)), float(scale), dtype_code(q.dtype),
+                stream.cuda_stream)
+    if rc != 0:
+        raise FaError(rc, fa_status_string(rc))
+    return dq, dk, dv

@@ -1,8 +1,9 @@
 """ctypes binding of libfa.so: argument marshalling only.
 
-The names match the C ABI in include/fa.h (``fa_fwd``, ``fa_status_string``,
-``fa_kernel_name``, ``fa_version``).  Every step of the attention forward
-runs in the HIP kernels; there is no Python or CPU fallback, and loading
+The names match the C ABI in include/fa.h (``fa_fwd``, ``fa_bwd``,
+``fa_status_string``, ``fa_kernel_name``, ``fa_bwd_kernel_name``,
+``fa_version``).  Every step of the attention forward and backward runs in
+the HIP kernels; there is no Python or CPU fallback, and loading
 fails loudly when the library has not been built.
 """
 from __future__ import annotations
@@ -45,6 +46,12 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                            ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [vp] * 10 + [i64] * 5 + [
+        ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_kernel_name.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
+                                       ctypes.c_float, ctypes.c_int]
+    lib.fa_bwd_kernel_name.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_kernel_name.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
@@ -62,6 +69,22 @@ def fa_fwd(q: int, k: int, v: int, o: int, lse: int | None, B: int, H: int,
     """Raw call: integer device addresses in, status code out."""
     return load().fa_fwd(q, k, v, o, lse, B, H, Lq, Lk, D, int(causal),
                          float(scale), int(dtype), stream)
+
+
+def fa_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int,
+           dk: int, dv: int, delta: int, B: int, H: int, Lq: int, Lk: int,
+           D: int, causal: int, scale: float, dtype: int,
+           stream: int | None) -> int:
+    """Raw call: integer device addresses in, status code out."""
+    return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Lq,
+                         Lk, D, int(causal), float(scale), int(dtype), stream)
+
+
+def fa_bwd_kernel_name(B: int, H: int, Lq: int, Lk: int, D: int, causal: int,
+                       scale: float, dtype: int) -> str | None:
+    r = load().fa_bwd_kernel_name(B, H, Lq, Lk, D, int(causal), float(scale),
+                                  int(dtype))
+    return None if r is None else r.decode()
 
 
 def fa_status_string(status: int) -> str:

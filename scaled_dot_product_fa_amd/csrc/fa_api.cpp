@@ -141,17 +141,85 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+           const void *dout, void *dq, void *dk, void *dv, float *delta, int64_t B, int64_t H,
+           int64_t Lq, int64_t Lk, int64_t D, int causal, float scale, int dtype, void *stream)
+{
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
+        dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || delta == nullptr)
+        return FA_ERR_NULL;
+    int rc = check_args(B, H, Lq, Lk, D, scale, dtype);
+    if (rc != FA_OK) return rc;
+    // the key-block grid B*H*ceil(Lk/32) must fit a 31-bit launch as well
+    if (B * H * ((Lk + 31) / 32) > (int64_t)0x7fffffff) return FA_ERR_SHAPE;
+
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
+                          reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq) |
+                          reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv);
+    if ((mis & 15u) != 0 ||
+        ((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(delta)) & 3u) != 0)
+        return FA_ERR_ALIGN;
+
+    const int64_t es = dtype == FA_F32 ? 4 : 2;
+    const int64_t nq = B * H * Lq * D * es, nk = B * H * Lk * D * es, nl = B * H * Lq * 4;
+    const void *ins[6] = {q, k, v, o, lse, dout};
+    const int64_t in_n[6] = {nq, nk, nk, nq, nl, nq};
+    void *outs[4] = {dq, dk, dv, delta};
+    const int64_t out_n[4] = {nq, nk, nk, nl};
+    for (int w = 0; w < 4; ++w) {
+        for (int r = 0; r < 6; ++r)
+            if (overlaps(outs[w], out_n[w], ins[r], in_n[r])) return FA_ERR_ALIAS;
+        for (int u = w + 1; u < 4; ++u)
+            if (overlaps(outs[w], out_n[w], outs[u], out_n[u])) return FA_ERR_ALIAS;
+    }
+
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) {
+        (void)hipGetLastError();
+        return FA_ERR_POINTER;
+    }
+    for (int r = 0; r < 6; ++r)
+        if (!is_device_ptr(ins[r], device)) return FA_ERR_POINTER;
+    for (int w = 0; w < 4; ++w)
+        if (!is_device_ptr(outs[w], device)) return FA_ERR_POINTER;
+
+    fa::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = delta;
+    a.B = B;
+    a.H = H;
+    a.Lq = Lq;
+    a.Lk = Lk;
+    a.D = D;
+    a.causal = causal ? 1 : 0;
+    a.scale = scale;
+    a.dtype = dtype;
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = fa::bwd_delta_launch(a);
+    if (e == hipSuccess) e = fa::bwd_valu_launch(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char *fa_status_string(int status)
 {
     switch (status) {
     case FA_OK: return "ok";
-    case FA_ERR_NULL: return "q, k, v or o is NULL";
+    case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, H, Lq or Lk out of range";
     case FA_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
     case FA_ERR_DTYPE: return "dtype must be FA_F32, FA_F16 or FA_BF16";
     case FA_ERR_SCALE: return "scale must be finite";
-    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-    case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA_ERR_ALIGN: return "tensors must be 16-byte aligned, lse and delta 4-byte aligned";
+    case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_POINTER: return "a pointer is not device memory of the current device";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
@@ -172,6 +240,23 @@ const char *fa_kernel_name(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t
     return fa::valu_kernel_name(a);
 }
 
-int fa_version(void) { return 100; }
+const char *fa_bwd_kernel_name(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                               int causal, float scale, int dtype)
+{
+    if (check_args(B, H, Lq, Lk, D, scale, dtype) != FA_OK) return nullptr;
+    if (B * H * ((Lk + 31) / 32) > (int64_t)0x7fffffff) return nullptr;
+    fa::BwdArgs a{};
+    a.B = B;
+    a.H = H;
+    a.Lq = Lq;
+    a.Lk = Lk;
+    a.D = D;
+    a.causal = causal ? 1 : 0;
+    a.scale = scale;
+    a.dtype = dtype;
+    return fa::bwd_valu_kernel_name(a);
+}
+
+int fa_version(void) { return 200; }
 
 }  // extern "C"

@@ -41,4 +41,24 @@ hipError_t mfma_launch(const FwdArgs &a, const MfmaTile &t);
 const char *valu_kernel_name(const FwdArgs &a);
 hipError_t valu_launch(const FwdArgs &a);
 
+// Arguments of one backward call after validation.
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    void *dq, *dk, *dv;
+    float *delta;
+    int64_t B, H, Lq, Lk, D;
+    int causal;
+    float scale;
+    int dtype;
+    hipStream_t stream;
+};
+
+// delta_i = dO_i . O_i into a.delta (any I/O type).
+hipError_t bwd_delta_launch(const BwdArgs &a);
+
+// Vector-ALU backward (dK, dV, then dQ): any I/O type, D in {64, 128}.
+const char *bwd_valu_kernel_name(const BwdArgs &a);
+hipError_t bwd_valu_launch(const BwdArgs &a);
+
 }  // namespace fa

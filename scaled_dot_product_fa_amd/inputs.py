@@ -95,6 +95,15 @@ def make_qkv(B: int, H: int, Lq: int, Lk: int, D: int, dtype: str = "bf16",
     return q.to(t), k.to(t), v.to(t)
 
 
+def make_dout(B: int, H: int, Lq: int, D: int, dtype: str = "bf16",
+              seed: int = 0):
+    """Seeded incoming gradient dO [B,H,Lq,D] (iid N(0, 1), cast RNE), from
+    its own generator so that q, k, v are the same draws as make_qkv's."""
+    g = torch.Generator("cpu").manual_seed(int(seed) * 2654435761 % (1 << 63) + 17)
+    return torch.randn((B, H, Lq, D), generator=g,
+                       dtype=torch.float32).to(DTYPES[dtype])
+
+
 def workload_inputs(w: Workload):
     """The seeded inputs of a named workload (CPU tensors)."""
     return make_qkv(w.B, w.H, w.Lq, w.Lk, w.D, w.dtype, w.seed, w.peaky_frac,

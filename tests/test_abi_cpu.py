@@ -23,8 +23,9 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_fwd", "fa_kernel_name",
-                                    "fa_status_string", "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_kernel_name", "fa_fwd",
+                                    "fa_kernel_name", "fa_status_string",
+                                    "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -128,4 +129,57 @@ def test_forward_rejects_host_tensors():
 
 
 def test_version():
-    assert fa.fa_version() >= 100
+    assert fa.fa_version() >= 200
+
+
+# ---- fa_bwd: the same host-side validation --------------------------------
+
+DO, DQ, DK, DV, DL = 6 << 40, 7 << 40, 8 << 40, 9 << 40, 10 << 40
+
+
+def bcall(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, delta=DL,
+          **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fa.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, a["B"], a["H"],
+                     a["Lq"], a["Lk"], a["D"], a["causal"], a["scale"],
+                     a["dtype"], None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse", "dout", "dq",
+                                   "dk", "dv", "delta"])
+def test_bwd_null_pointer(which):
+    assert bcall(**{which: None}) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 2), (dict(Lk=0), 2), (dict(Lq=(1 << 24) + 1), 2),
+    (dict(D=96), 3), (dict(dtype=3), 4), (dict(scale=float("nan")), 5),
+])
+def test_bwd_bad_arguments(kw, code):
+    assert bcall(**kw) == code
+
+
+def test_bwd_misaligned_and_aliased():
+    assert bcall(dout=DO + 8) == 6
+    assert bcall(dk=DK + 2) == 6
+    assert bcall(delta=DL + 2) == 6
+    nbytes = 1 * 2 * 128 * 64 * 2
+    assert bcall(dq=Q) == 7                   # dq on top of q
+    assert bcall(dv=O + nbytes - 16) == 7     # dv overlapping the tail of o
+    assert bcall(dk=DV + 64) == 7             # two outputs overlapping
+    assert bcall(delta=L) == 7                # delta on top of lse
+    assert bcall(delta=DQ + 16) == 7          # delta inside dq
+
+
+def test_bwd_non_device_pointers_rejected_without_gpu():
+    buf = [ctypes.create_string_buffer(1 << 16) for _ in range(10)]
+    a = [((ctypes.addressof(b) + 15) // 16) * 16 for b in buf]
+    assert bcall(*a) == 8
+
+
+def test_bwd_kernel_selection():
+    assert fa.fa_bwd_kernel_name(1, 2, 128, 128, 64, 1, 0.125, 0) == \
+        "fa_bwd_valu_f32_d64_causal"
+    assert fa.fa_bwd_kernel_name(1, 2, 128, 128, 65, 0, 1.0, 2) is None
+    assert fa.fa_bwd_kernel_name(1, 2, 128, 0, 64, 0, 1.0, 2) is None

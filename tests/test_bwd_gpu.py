@@ -1,0 +1,112 @@
+"""GPU parity of the backward: fa_bwd (through the C ABI) against the oracle's
+fp64 chain-rule gradients.
+
+Gradients are far from unit scale (for N(0, 1) inputs dV_j is about
+sqrt(e / Lq)), so the stated max-abs bars (2e-2 for bf16/fp16 I/O, 1e-5 for
+fp32) are applied to the error divided by the largest reference magnitude of
+that tensor: max|g - ref| <= tol * max|ref|.  The bf16/fp16 kernels round the
+probabilities and ds to the I/O type before they multiply tensors (relative
+error 2^-8 for bf16, 2^-11 for fp16), which gives a normalised error of a few
+1e-3 at most; a wrong term (a dropped delta, a missing scale, a transposed
+operand) gives an error of order one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scaled_dot_product_fa_amd as fa
+from scaled_dot_product_fa_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to64(t):
+    return t.to(torch.float64).numpy()
+
+
+def run_gpu(q, k, v, g, causal, scale):
+    dev = torch.device("cuda:0")
+    q, k, v, g = (t.to(dev) for t in (q, k, v, g))
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    delta = torch.empty(lse.shape, device=dev, dtype=torch.float32)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, g, causal=causal, scale=scale,
+                             delta=delta)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu(), delta.cpu()
+
+
+def norm_err(a, ref):
+    return float(np.abs(to64(a) - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def check(B, H, Lq, Lk, D, dt, causal, scale=None, seed=0, label=""):
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    q, k, v = inputs.make_qkv(B, H, Lq, Lk, D, dt, seed)
+    g = inputs.make_dout(B, H, Lq, D, dt, seed)
+    name = fa.fa_bwd_kernel_name(B, H, Lq, Lk, D, int(causal), scale,
+                                 fa.dtype_code(q.dtype))
+    say(f"[bwd] {label} B={B} H={H} Lq={Lq} Lk={Lk} D={D} {dt} "
+        f"causal={causal} scale={scale:.5g} kernel={name}")
+    dq, dk, dv, delta = run_gpu(q, k, v, g, causal, scale)
+    rq, rk, rv, rd = oracle.attention_bwd(to64(q), to64(k), to64(v), to64(g),
+                                          causal, scale, with_delta=True)
+    errs = {n: norm_err(a, r) for n, a, r in (("dq", dq, rq), ("dk", dk, rk),
+                                             ("dv", dv, rv), ("delta", delta, rd))}
+    say("[bwd]   " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for t in (dq, dk, dv, delta):
+        assert torch.isfinite(t.float()).all()
+    for n, e in errs.items():
+        assert e <= TOL[dt], (n, e)
+    return errs
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+def test_tiny_workload(causal):
+    w = inputs.CONFIGS["tiny"]
+    check(w.B, w.H, w.Lq, w.Lk, w.D, w.dtype, causal, w.scale, w.seed, "tiny")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+def test_small_workload(causal):
+    w = inputs.CONFIGS["small"]
+    check(w.B, w.H, w.Lq, w.Lk, w.D, w.dtype, causal, w.scale, w.seed, "small")
+
+
+RAGGED = [(1, 2, 200, 333, 128, "bf16"), (2, 1, 77, 45, 64, "f16"),
+          (1, 1, 300, 100, 64, "bf16"), (1, 1, 1, 1, 128, "bf16"),
+          (1, 2, 1, 257, 64, "f16"), (1, 1, 257, 1, 128, "bf16"),
+          (1, 1, 130, 190, 128, "f32"), (1, 3, 95, 64, 64, "f32")]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+def test_ragged(shape, causal):
+    B, H, Lq, Lk, D, dt = shape
+    check(B, H, Lq, Lk, D, dt, causal, seed=Lq + Lk + D, label="ragged")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 0.9])
+def test_other_scales(scale):
+    check(1, 2, 96, 150, 64, "bf16", True, scale=scale, seed=5, label="scale")
+
+
+def test_deterministic():
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inputs.make_qkv(1, 4, 333, 300, 128, "bf16", 9))
+    g = inputs.make_dout(1, 4, 333, 128, "bf16", 9).to(dev)
+    o, lse = fa.forward(q, k, v, causal=True)
+    a = fa.backward(q, k, v, o, lse, g, causal=True)
+    b = fa.backward(q, k, v, o, lse, g, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
