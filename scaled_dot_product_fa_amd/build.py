@@ -23,7 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_mfma.hip", "fa_valu.hip", "fa_bwd_valu.hip"]
+SOURCES = ["fa_api.cpp", "fa_mfma.hip", "fa_valu.hip", "fa_bwd_valu.hip",
+           "fa_bwd_mfma.hip"]
 ARCH = "gfx950"
 
 

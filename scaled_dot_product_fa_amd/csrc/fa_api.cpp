@@ -204,8 +204,13 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     a.scale = scale;
     a.dtype = dtype;
     a.stream = static_cast<hipStream_t>(stream);
+    fa::MfmaTile unused{};
+    bool force_valu = false;
+    (void)env_tile(unused, force_valu);
     hipError_t e = fa::bwd_delta_launch(a);
-    if (e == hipSuccess) e = fa::bwd_valu_launch(a);
+    if (e == hipSuccess)
+        e = (!force_valu && fa::bwd_mfma_supported(a)) ? fa::bwd_mfma_launch(a)
+                                                        : fa::bwd_valu_launch(a);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -254,6 +259,10 @@ const char *fa_bwd_kernel_name(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int
     a.causal = causal ? 1 : 0;
     a.scale = scale;
     a.dtype = dtype;
+    fa::MfmaTile unused{};
+    bool force_valu = false;
+    (void)env_tile(unused, force_valu);
+    if (!force_valu && fa::bwd_mfma_supported(a)) return fa::bwd_mfma_kernel_name(a);
     return fa::bwd_valu_kernel_name(a);
 }
 

@@ -1,0 +1,592 @@
+// fa_bwd_mfma.hip -- attention backward for gfx950 on bf16/fp16 MFMA.
+//
+// Gradients of O = softmax(scale Q K^T [+causal]) V for an incoming dO, by
+// the chain rule through that definition, with the probabilities recomputed
+// from the forward's row statistic lse rather than stored (the
+// FlashAttention-2 forward article keeps Q, K, V, O and the statistic for the
+// backward, and its account of the IO-aware idea notes that the backward may
+// recompute instead of store):
+//
+//   p_ij = exp(scale q_i.k_j - lse_i),  ds_ij = p_ij (dO_i.v_j - delta_i),
+//   dV_j = sum_i p_ij dO_i,  dK_j = scale sum_i ds_ij q_i,
+//   dQ_i = scale sum_j ds_ij k_j,  delta_i = dO_i . O_i (computed beforehand).
+//
+// Two kernels, no atomics (so the result is deterministic):
+//
+//   * dK/dV kernel, one workgroup per block of keys.  Each wave owns 32 keys
+//     and keeps their K and V rows in VGPRs as MFMA B operands.  Tiles of 32
+//     query rows of Q and dO stream through LDS (double-buffered, staged
+//     through VGPRs).  Per tile: S = Q K^T and dP = dO V^T on
+//     v_mfma_f32_32x32x16_{bf16,f16} with the Q/dO rows read in a permuted
+//     order (bits 2 and 3 of the row swapped), so each lane's accumulator
+//     holds one key column and two runs of 8 consecutive queries.  P and dS,
+//     rounded to the I/O type, are then directly the B operands of
+//     dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T come from the same LDS
+//     tiles through ds_read_b64_tr_b16 (transposing reads).
+//   * dQ kernel, one workgroup per block of query rows, the forward's layout:
+//     each wave owns 32 queries with Q^T and dO^T in VGPRs; tiles of 64 keys
+//     of K and V stream through LDS; S^T = K Q^T and dP^T = V dO^T put one
+//     query column in each lane; dS^T is the B operand of dQ^T += K^T dS^T,
+//     K^T read from the K tile with transposing reads.
+//
+// The LDS tiles are row-major with 16-byte chunks XOR-swizzled by row with a
+// pattern that keeps both the permuted row reads and the transposing reads
+// free of bank conflicts.  exp uses exp2 with scale*log2(e) folded into one
+// FMA.  Causal tiles that a wave cannot see are skipped; only tiles on the
+// diagonal are masked (key j kept for query i when j <= i).
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kThreads = 256;   // 4 waves per workgroup
+
+struct Bf16Ops {
+    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float x, float y)
+    {
+        bf16x2 r = {(__bf16)x, (__bf16)y};
+        return __builtin_bit_cast(uint32_t, r);
+    }
+};
+
+struct F16Ops {
+    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float x, float y)
+    {
+        f16x2 r = {(_Float16)x, (_Float16)y};
+        return __builtin_bit_cast(uint32_t, r);
+    }
+};
+
+// Swap bits 2 and 3 of a row index within a 32-row block.  Reading A rows
+// in this order makes accumulator element r of lane l belong to row
+// 8*(l/32) + r (r < 8) or 16 + 8*(l/32) + (r - 8) (r >= 8).
+__device__ __forceinline__ int swap_bits23(int r)
+{
+    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Row index (0..31) of accumulator element r of a lane in half `hi`.
+__device__ __forceinline__ int acc_row(int r, int hi)
+{
+    return r < 8 ? 8 * hi + r : 16 + 8 * hi + (r - 8);
+}
+
+// Chunk swizzle shared by every tile (64 LDS banks of 4 bytes).
+//  * Permuted row reads (16 bytes per lane): a phase of 16 lanes reads rows
+//    swap_bits23(0..15) at one logical chunk, so the swizzle must be a
+//    bijection on rows mod 16 (D = 128, 256-byte rows) or, for D = 64
+//    (128-byte rows, row parity picks the bank half), on the 8 rows of each
+//    parity.
+//  * Transposing reads (8 bytes per lane): a phase of 32 lanes reads 4
+//    consecutive rows x 4 adjacent chunks; the 4 rows must land in distinct
+//    4-chunk groups (D = 128), or rows r and r+2 must (D = 64).
+// D = 128: f(r) = 4*(r%4) + (r/4)%4.  D = 64: x = (r/2)%8, f = 4*(x%2) + x/2.
+template <int D>
+__device__ __forceinline__ int swz(int row)
+{
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    const int x = (row >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+}
+
+__device__ __forceinline__ uint2 ds_read_tr(const uint8_t *p)
+{
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct BwdParams {
+    const uint16_t *q, *k, *v, *dout;
+    const float *lse, *delta;
+    uint16_t *dq, *dk, *dv;
+    int BH, Lq, Lk, nt;
+    float scale, c;  // c = scale * log2(e)
+};
+
+// Workgroup id -> (head bh, block t of nt per head).  Hardware places
+// workgroup w on XCD w % 8; consecutive logical ids share an XCD, so one
+// head's blocks (which stream the same tensors) share an L2.  Causal grids
+// start with the longest blocks: low t when heavy_low, else high t.
+__device__ __forceinline__ void decompose(int wg, int nwg, int BH, int nt, bool causal,
+                                          bool heavy_low, int &bh, int &t)
+{
+    const int per = nwg >> 3, rem = nwg & 7;
+    const int xcd = wg & 7, idx = wg >> 3;
+    if (causal && (BH & 7) == 0) {
+        const int hpx = BH >> 3;
+        const int rank = idx / hpx;
+        t = heavy_low ? rank : nt - 1 - rank;
+        bh = xcd * hpx + idx % hpx;
+        return;
+    }
+    const int logical = xcd < rem ? xcd * (per + 1) + idx
+                                  : rem * (per + 1) + (xcd - rem) * per + idx;
+    bh = logical / nt;
+    t = logical % nt;
+    if (causal && !heavy_low) t = nt - 1 - t;
+}
+
+// Per-lane LDS offsets of the transposing read: A operand [32 dims x 16
+// rows] of block db, rows 8*hi..8*hi+3 (first read) and +4 (second read) of
+// a 16-row chunk; add chunk * 16 * ROWB (the swizzle repeats every 16 rows).
+template <int D, int DB>
+__device__ __forceinline__ void tr_offsets(int lane, uint32_t (&off)[DB][2])
+{
+    constexpr int ROWB = D * 2;
+    const int hi = lane >> 5, g = lane >> 4, t = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 8 * hi + (t >> 2) + 4 * h;
+            const int col = db * 32 + 16 * (g & 1) + 4 * (t & 3);
+            const int c = col >> 3, within = (col & 7) * 2;
+            off[db][h] = (uint32_t)(row * ROWB + ((c ^ swz<D>(row)) * 16) + within);
+        }
+}
+
+template <int DB>
+__device__ __forceinline__ u32x4 read_tr(const uint8_t *tile, const uint32_t (&off)[DB][2],
+                                         int db, uint32_t chunk_off)
+{
+    const uint2 lo = ds_read_tr(tile + off[db][0] + chunk_off);
+    const uint2 hi4 = ds_read_tr(tile + off[db][1] + chunk_off);
+    return u32x4{lo.x, lo.y, hi4.x, hi4.y};
+}
+
+// Store a 32(dims) x 32(columns) accumulator block: the lane owns column
+// l32 and dims 32*db + 8*g + 4*hi + (0..3) for g = 0..3.
+template <typename Ops>
+__device__ __forceinline__ void store_cols(uint16_t *row_base, int db, int hi, const f32x16 &acc,
+                                           float mul)
+{
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        uint2 w;
+        w.x = Ops::pack2(acc[4 * g] * mul, acc[4 * g + 1] * mul);
+        w.y = Ops::pack2(acc[4 * g + 2] * mul, acc[4 * g + 3] * mul);
+        *(uint2 *)(row_base + db * 32 + 8 * g + 4 * hi) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per 128 keys, 32 per wave; query tiles of 32 rows.
+// ---------------------------------------------------------------------------
+template <typename Ops, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkdv_mfma_kernel(BwdParams p)
+{
+    constexpr int NW = kThreads / 64;
+    constexpr int BK = NW * 32;          // keys per workgroup
+    constexpr int BQ = 32;               // query rows per tile
+    constexpr int DC = D / 16, DB = D / 32;
+    constexpr int ROWB = D * 2;
+    constexpr int CH = D / 8;            // 16-byte chunks per row
+    constexpr int TILEB = BQ * ROWB;
+    constexpr int NLD = BQ * CH / kThreads;   // chunks per thread per tensor
+    constexpr int BUFB = 2 * TILEB + 2 * BQ * 4;
+    static_assert(NLD >= 1 && BQ * CH % kThreads == 0, "tile split");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUFB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    int bh, kt;
+    decompose(blockIdx.x, gridDim.x, p.BH, p.nt, CAUSAL, true, bh, kt);
+    const int Lq = p.Lq, Lk = p.Lk;
+    const int k_first = kt * BK;
+    const int kw = k_first + wave * 32;
+    const int key = kw + l32;
+
+    const uint16_t *qh = p.q + (int64_t)bh * Lq * D;
+    const uint16_t *gh = p.dout + (int64_t)bh * Lq * D;
+    const float *lh = p.lse + (int64_t)bh * Lq;
+    const float *dh = p.delta + (int64_t)bh * Lq;
+
+    // K and V rows of this lane's key: B operands of S = Q K^T, dP = dO V^T
+    u32x4 kop[DC], vop[DC];
+    {
+        const uint16_t *kr = p.k + ((int64_t)bh * Lk + key) * D + 8 * hi;
+        const uint16_t *vr = p.v + ((int64_t)bh * Lk + key) * D + 8 * hi;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+            kop[dc] = key < Lk ? *(const u32x4 *)(kr + dc * 16) : u32x4{0u, 0u, 0u, 0u};
+            vop[dc] = key < Lk ? *(const u32x4 *)(vr + dc * 16) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            dk[db][i] = 0.f;
+            dv[db][i] = 0.f;
+        }
+
+    // staging: thread -> (row, chunk) pairs of a tile
+    int st_row[NLD];
+    uint32_t st_g[NLD], st_l[NLD];
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+        const int idx = tid + n * kThreads;
+        const int row = idx / CH, pc = idx % CH;
+        st_row[n] = row;
+        st_g[n] = (uint32_t)(row * D + pc * 8);
+        st_l[n] = (uint32_t)(row * ROWB + ((pc ^ swz<D>(row)) * 16));
+    }
+    // permuted row reads (A of S and dP) and transposing reads (A of dV^T, dK^T)
+    uint32_t rd_row[DC];
+    {
+        const int row = swap_bits23(l32);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+            rd_row[dc] = (uint32_t)(row * ROWB + (((2 * dc + hi) ^ swz<D>(row)) * 16));
+    }
+    uint32_t rd_tr[DB][2];
+    tr_offsets<D, DB>(lane, rd_tr);
+
+    const int i_begin = CAUSAL ? k_first : 0;   // rows above the block see none of its keys
+    const int ntiles = i_begin < Lq ? (Lq - i_begin + BQ - 1) / BQ : 0;
+
+    u32x4 stq[NLD], stg[NLD];
+    float st_x = 0.f;
+    auto fetch = [&](int i0) {
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) {
+            const bool ok = i0 + st_row[n] < Lq;
+            const int64_t o = (int64_t)i0 * D + st_g[n];
+            stq[n] = ok ? *(const u32x4 *)(qh + o) : u32x4{0u, 0u, 0u, 0u};
+            stg[n] = ok ? *(const u32x4 *)(gh + o) : u32x4{0u, 0u, 0u, 0u};
+        }
+        if (tid < 2 * BQ) {
+            const int i = i0 + (tid & (BQ - 1));
+            // rows past the end: lse = +inf makes their probabilities 0
+            if (tid < BQ) st_x = i < Lq ? lh[i] * kLog2e : INFINITY;
+            else st_x = i < Lq ? dh[i] : 0.f;
+        }
+    };
+    auto stage = [&](uint8_t *buf) {
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) {
+            *(u32x4 *)(buf + st_l[n]) = stq[n];
+            *(u32x4 *)(buf + TILEB + st_l[n]) = stg[n];
+        }
+        if (tid < 2 * BQ) ((float *)(buf + 2 * TILEB))[tid] = st_x;
+    };
+
+    if (ntiles > 0) {
+        fetch(i_begin);
+        stage(smem);
+        __syncthreads();
+    }
+    for (int t = 0; t < ntiles; ++t) {
+        const int i0 = i_begin + t * BQ;
+        const uint8_t *cur = smem + (t & 1) * BUFB;
+        uint8_t *nxt = smem + ((t + 1) & 1) * BUFB;
+        const bool more = t + 1 < ntiles;
+        if (more) fetch(i0 + BQ);
+        // causal: this wave's keys are invisible to the whole tile when
+        // i0 + 31 < kw; the tile needs a mask only on the diagonal (i0 == kw)
+        if (!CAUSAL || i0 + BQ - 1 >= kw) {
+            const uint8_t *qt = cur, *gt = cur + TILEB;
+            const float *lt = (const float *)(cur + 2 * TILEB), *dlt = lt + BQ;
+            f32x16 s, dp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[i] = 0.f;
+                dp[i] = 0.f;
+            }
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc) {
+                s = Ops::mma(*(const u32x4 *)(qt + rd_row[dc]), kop[dc], s);
+                dp = Ops::mma(*(const u32x4 *)(gt + rd_row[dc]), vop[dc], dp);
+            }
+            float pv[16], dsv[16];
+            const bool diag = CAUSAL && i0 == kw;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = acc_row(r, hi);
+                float e = exp2_fast(fmaf(s[r], p.c, -lt[row]));
+                if (diag) e = l32 <= row ? e : 0.f;
+                pv[r] = e;
+                dsv[r] = e * (dp[r] - dlt[row]);
+            }
+            u32x4 pk[2], dsk[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    pk[h][w] = Ops::pack2(pv[8 * h + 2 * w], pv[8 * h + 2 * w + 1]);
+                    dsk[h][w] = Ops::pack2(dsv[8 * h + 2 * w], dsv[8 * h + 2 * w + 1]);
+                }
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                const uint32_t co = (uint32_t)(kc * 16 * ROWB);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dv[db] = Ops::mma(read_tr<DB>(gt, rd_tr, db, co), pk[kc], dv[db]);
+                    dk[db] = Ops::mma(read_tr<DB>(qt, rd_tr, db, co), dsk[kc], dk[db]);
+                }
+            }
+        }
+        if (more) stage(nxt);
+        __syncthreads();
+    }
+
+    if (key < Lk) {
+        uint16_t *dkr = p.dk + ((int64_t)bh * Lk + key) * D;
+        uint16_t *dvr = p.dv + ((int64_t)bh * Lk + key) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            store_cols<Ops>(dkr, db, hi, dk[db], p.scale);
+            store_cols<Ops>(dvr, db, hi, dv[db], 1.f);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per 128 query rows, 32 per wave; key tiles of 64.
+// ---------------------------------------------------------------------------
+template <typename Ops, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dq_mfma_kernel(BwdParams p)
+{
+    constexpr int NW = kThreads / 64;
+    constexpr int BM = NW * 32;          // query rows per workgroup
+    constexpr int BN = 64;               // keys per tile
+    constexpr int KB = BN / 32, KC = BN / 16;
+    constexpr int DC = D / 16, DB = D / 32;
+    constexpr int ROWB = D * 2;
+    constexpr int CH = D / 8;
+    constexpr int TILEB = BN * ROWB;
+    constexpr int NLD = BN * CH / kThreads;
+    constexpr int BUFB = 2 * TILEB;
+    static_assert(NLD >= 1 && BN * CH % kThreads == 0, "tile split");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUFB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    int bh, qt;
+    decompose(blockIdx.x, gridDim.x, p.BH, p.nt, CAUSAL, false, bh, qt);
+    const int Lq = p.Lq, Lk = p.Lk;
+    const int q_first = qt * BM;
+    const int qw = q_first + wave * 32;
+    const int qrow = qw + l32;
+    const bool row_ok = qrow < Lq;
+
+    const uint16_t *kh = p.k + (int64_t)bh * Lk * D;
+    const uint16_t *vh = p.v + (int64_t)bh * Lk * D;
+
+    // Q^T and dO^T operands (B of S^T = K Q^T and dP^T = V dO^T)
+    u32x4 qop[DC], gop[DC];
+    {
+        const uint16_t *qr = p.q + ((int64_t)bh * Lq + qrow) * D + 8 * hi;
+        const uint16_t *gr = p.dout + ((int64_t)bh * Lq + qrow) * D + 8 * hi;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+            qop[dc] = row_ok ? *(const u32x4 *)(qr + dc * 16) : u32x4{0u, 0u, 0u, 0u};
+            gop[dc] = row_ok ? *(const u32x4 *)(gr + dc * 16) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    const float lse2 = row_ok ? p.lse[(int64_t)bh * Lq + qrow] * kLog2e : INFINITY;
+    const float dl = row_ok ? p.delta[(int64_t)bh * Lq + qrow] : 0.f;
+    f32x16 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+
+    int st_row[NLD];
+    uint32_t st_g[NLD], st_l[NLD];
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+        const int idx = tid + n * kThreads;
+        const int row = idx / CH, pc = idx % CH;
+        st_row[n] = row;
+        st_g[n] = (uint32_t)(row * D + pc * 8);
+        st_l[n] = (uint32_t)(row * ROWB + ((pc ^ swz<D>(row)) * 16));
+    }
+    uint32_t rd_row[DC];
+    {
+        const int row = swap_bits23(l32);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+            rd_row[dc] = (uint32_t)(row * ROWB + (((2 * dc + hi) ^ swz<D>(row)) * 16));
+    }
+    uint32_t rd_tr[DB][2];
+    tr_offsets<D, DB>(lane, rd_tr);
+
+    const int kv_end = CAUSAL ? min(Lk, q_first + BM) : Lk;
+    const int ntiles = (kv_end + BN - 1) / BN;
+
+    u32x4 stk[NLD], stv[NLD];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) {
+            const bool ok = k0 + st_row[n] < Lk;
+            const int64_t o = (int64_t)k0 * D + st_g[n];
+            stk[n] = ok ? *(const u32x4 *)(kh + o) : u32x4{0u, 0u, 0u, 0u};
+            stv[n] = ok ? *(const u32x4 *)(vh + o) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto stage = [&](uint8_t *buf) {
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) {
+            *(u32x4 *)(buf + st_l[n]) = stk[n];
+            *(u32x4 *)(buf + TILEB + st_l[n]) = stv[n];
+        }
+    };
+
+    if (ntiles > 0) {
+        fetch(0);
+        stage(smem);
+        __syncthreads();
+    }
+    for (int t = 0; t < ntiles; ++t) {
+        const int k0 = t * BN;
+        const uint8_t *cur = smem + (t & 1) * BUFB;
+        uint8_t *nxt = smem + ((t + 1) & 1) * BUFB;
+        const bool more = t + 1 < ntiles;
+        if (more) fetch(k0 + BN);
+        if (!CAUSAL || k0 <= qw + 31) {
+            const uint8_t *kt = cur, *vt = cur + TILEB;
+            // mask: keys past the diagonal (causal) or past the end
+            const bool need_mask = (CAUSAL && k0 + BN - 1 > qw) || k0 + BN > Lk;
+            u32x4 dsk[KC];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                f32x16 s, dp;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    s[i] = 0.f;
+                    dp[i] = 0.f;
+                }
+                const uint32_t bo = (uint32_t)(kb * 32 * ROWB);
+#pragma unroll
+                for (int dc = 0; dc < DC; ++dc) {
+                    s = Ops::mma(*(const u32x4 *)(kt + bo + rd_row[dc]), qop[dc], s);
+                    dp = Ops::mma(*(const u32x4 *)(vt + bo + rd_row[dc]), gop[dc], dp);
+                }
+                float dsv[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float e = exp2_fast(fmaf(s[r], p.c, -lse2));
+                    if (need_mask) {
+                        const int j = k0 + kb * 32 + acc_row(r, hi);
+                        e = (j < Lk && (!CAUSAL || j <= qrow)) ? e : 0.f;
+                    }
+                    dsv[r] = e * (dp[r] - dl);
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        dsk[2 * kb + h][w] =
+                            Ops::pack2(dsv[8 * h + 2 * w], dsv[8 * h + 2 * w + 1]);
+            }
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const uint32_t co = (uint32_t)(kc * 16 * ROWB);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    dq[db] = Ops::mma(read_tr<DB>(kt, rd_tr, db, co), dsk[kc], dq[db]);
+            }
+        }
+        if (more) stage(nxt);
+        __syncthreads();
+    }
+
+    if (row_ok) {
+        uint16_t *dqr = p.dq + ((int64_t)bh * Lq + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) store_cols<Ops>(dqr, db, hi, dq[db], p.scale);
+    }
+}
+
+template <typename Ops, int D, bool CAUSAL>
+hipError_t launch_t(const BwdArgs &a)
+{
+    BwdParams p;
+    p.q = static_cast<const uint16_t *>(a.q);
+    p.k = static_cast<const uint16_t *>(a.k);
+    p.v = static_cast<const uint16_t *>(a.v);
+    p.dout = static_cast<const uint16_t *>(a.dout);
+    p.lse = a.lse;
+    p.delta = a.delta;
+    p.dq = static_cast<uint16_t *>(a.dq);
+    p.dk = static_cast<uint16_t *>(a.dk);
+    p.dv = static_cast<uint16_t *>(a.dv);
+    p.BH = (int)(a.B * a.H);
+    p.Lq = (int)a.Lq;
+    p.Lk = (int)a.Lk;
+    p.scale = a.scale;
+    p.c = a.scale * kLog2e;
+    constexpr int BLK = (kThreads / 64) * 32;
+    p.nt = (int)((a.Lk + BLK - 1) / BLK);
+    hipLaunchKernelGGL((fa_bwd_dkdv_mfma_kernel<Ops, D, CAUSAL>),
+                       dim3((unsigned)(p.BH * p.nt)), dim3(kThreads), 0, a.stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.nt = (int)((a.Lq + BLK - 1) / BLK);
+    hipLaunchKernelGGL((fa_bwd_dq_mfma_kernel<Ops, D, CAUSAL>),
+                       dim3((unsigned)(p.BH * p.nt)), dim3(kThreads), 0, a.stream, p);
+    return hipGetLastError();
+}
+
+template <typename Ops>
+hipError_t launch_ops(const BwdArgs &a)
+{
+    if (a.D == 64) return a.causal ? launch_t<Ops, 64, true>(a) : launch_t<Ops, 64, false>(a);
+    return a.causal ? launch_t<Ops, 128, true>(a) : launch_t<Ops, 128, false>(a);
+}
+
+}  // namespace
+
+bool bwd_mfma_supported(const BwdArgs &a)
+{
+    return (a.dtype == 1 || a.dtype == 2) && (a.D == 64 || a.D == 128);
+}
+
+hipError_t bwd_mfma_launch(const BwdArgs &a)
+{
+    return a.dtype == 1 ? launch_ops<F16Ops>(a) : launch_ops<Bf16Ops>(a);
+}
+
+const char *bwd_mfma_kernel_name(const BwdArgs &a)
+{
+    static const char *names[2][2][2] = {
+        {{"fa_bwd_mfma_f16_d64", "fa_bwd_mfma_f16_d64_causal"},
+         {"fa_bwd_mfma_f16_d128", "fa_bwd_mfma_f16_d128_causal"}},
+        {{"fa_bwd_mfma_bf16_d64", "fa_bwd_mfma_bf16_d64_causal"},
+         {"fa_bwd_mfma_bf16_d128", "fa_bwd_mfma_bf16_d128_causal"}},
+    };
+    return names[a.dtype == 2][a.D == 128][a.causal ? 1 : 0];
+}
+
+}  // namespace fa

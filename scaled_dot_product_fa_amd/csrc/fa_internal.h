@@ -57,6 +57,11 @@ struct BwdArgs {
 // delta_i = dO_i . O_i into a.delta (any I/O type).
 hipError_t bwd_delta_launch(const BwdArgs &a);
 
+// MFMA backward (dK/dV kernel, then dQ kernel): fp16/bf16 I/O, D in {64, 128}.
+bool bwd_mfma_supported(const BwdArgs &a);
+const char *bwd_mfma_kernel_name(const BwdArgs &a);
+hipError_t bwd_mfma_launch(const BwdArgs &a);
+
 // Vector-ALU backward (dK, dV, then dQ): any I/O type, D in {64, 128}.
 const char *bwd_valu_kernel_name(const BwdArgs &a);
 hipError_t bwd_valu_launch(const BwdArgs &a);
