@@ -1,6 +1,7 @@
-"""Attention forward throughput on one MI355X.
+"""Attention forward (and, with --backward, backward) throughput on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mid]
+    python bench.py --backward [--workload mid] [--causal]
 
 One step is one fa_fwd call (the whole forward: Q load, K/V stream, QK^T,
 masking, online softmax, PV, epilogue) over the workload's synthetic inputs,
@@ -16,6 +17,14 @@ rocprofv3 counter summary when it matches the current kernel source),
 same workload), ``parity`` (sampled rows of this run's output against the
 oracle) and, with --secondary, ``secondary`` (the 16K non-causal forward,
 the other shape the metric names).
+
+With --backward one step is one fa_bwd call (the delta, dK/dV and dQ kernels
+in order on one stream) over the same inputs plus a seeded dO, with o and lse
+from one forward call made before timing.  FLOPs per step are the
+algorithmic count of the five products (S, dP, dV, dK, dQ):
+10*B*H*Lq*Lk*D, halved when causal, i.e. 2.5x the forward's; the kernels
+recompute S and dP in both gradient kernels (7 products executed).  The
+roofline entry times the whole call with HIP events on its stream.
 """
 from __future__ import annotations
 
@@ -85,6 +94,94 @@ def time_forward(w, causal, steps, warmup):
                 kernel_ms=ev0.elapsed_time(ev1) / steps,
                 flops=w.flops(causal), bytes=w.io_bytes(), kernel=name,
                 q=q, k=k, v=v, o=o, lse=lse)
+
+
+def time_backward(w, causal, steps, warmup):
+    """Backward: dict with wall ms/step, event ms/call, flops and buffers."""
+    import torch
+    import scaled_dot_product_fa_amd as fa
+    from scaled_dot_product_fa_amd import inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v = inputs.workload_inputs(w)
+    g = inputs.make_dout(w.B, w.H, w.Lq, w.D, w.dtype, w.seed)
+    dq_, dk_, dv_, dg = q.to(dev), k.to(dev), v.to(dev), g.to(dev)
+    stream = torch.cuda.current_stream(dev)
+    o, lse = fa.forward(dq_, dk_, dv_, causal=causal, scale=w.scale, stream=stream)
+    gq, gk, gv = (torch.empty_like(t) for t in (dq_, dk_, dv_))
+    delta = torch.empty_like(lse)
+    name = fa.fa_bwd_kernel_name(w.B, w.H, w.Lq, w.Lk, w.D, int(causal), w.scale,
+                                 fa.dtype_code(dq_.dtype))
+    log(f"bench: backward {workload_desc(w, causal)} kernel={name} "
+        f"warmup={warmup} steps={steps}")
+
+    def step():
+        fa.backward(dq_, dk_, dv_, o, lse, dg, causal=causal, scale=w.scale,
+                    dq=gq, dk=gk, dv=gv, delta=delta, stream=stream)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    return dict(wall_ms=(t1 - t0) * 1e3 / steps,
+                kernel_ms=ev0.elapsed_time(ev1) / steps,
+                flops=2.5 * w.flops(causal), kernel=name,
+                q=q, k=k, v=v, g=g, dq=gq, dk=gk, dv=gv)
+
+
+def bwd_heads(w, n):
+    """n heads (b, h) spread over the workload, seeded order."""
+    step = max(1, (w.B * w.H) // n)
+    return [(bh // w.H, bh % w.H) for bh in range(0, w.B * w.H, step)][:n]
+
+
+def parity_bwd(w, causal, r):
+    """Gradients of one sampled head against the oracle (error / max|ref|)."""
+    import numpy as np
+    import torch
+    import oracle
+    f64 = lambda t: t.to(torch.float64).numpy()
+    (b, h), = bwd_heads(w, 1)[-1:]
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    ref = oracle.attention_bwd(f64(r["q"][sl]), f64(r["k"][sl]), f64(r["v"][sl]),
+                               f64(r["g"][sl]), causal, w.scale)
+    out = {"head": [b, h]}
+    for name, got, rr in zip(("dq", "dk", "dv"), (r["dq"], r["dk"], r["dv"]), ref):
+        out[f"err_{name}"] = float(np.abs(f64(got[sl].cpu()) - rr).max()
+                                   / max(np.abs(rr).max(), 1e-30))
+    return out
+
+
+def cpu_baseline_bwd(w, causal, r, budget_s=15.0):
+    """The fp64 oracle backward on whole heads of the same workload (heads are
+    independent), as many as fit the budget (at least one), scaled to
+    TFLOP/s with the same algorithmic FLOP formula per head."""
+    import torch
+    import oracle
+    f64 = lambda t: t.to(torch.float64).numpy()
+    per_head = 2.5 * w.flops(causal) / (w.B * w.H)
+    done, t_total = 0, 0.0
+    for b, h in bwd_heads(w, w.B * w.H):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        args = [f64(r[x][sl]) for x in ("q", "k", "v", "g")]
+        t0 = time.perf_counter()
+        oracle.attention_bwd(*args, causal, w.scale)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    return dict(value=done * per_head / t_total / 1e12, unit="TFLOP/s",
+                cores=oracle.num_threads(), kind="oracle",
+                sample=(f"{done} whole head(s) of {workload_desc(w, causal)} "
+                        f"backward, fp64, {t_total:.1f} s"),
+                seconds=t_total)
 
 
 def parity_rows(w, causal, r, n_random=8):
@@ -160,6 +257,8 @@ def main():
     ap.add_argument("--workload", default="mid")
     ap.add_argument("--causal", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time fa_bwd (gradients) instead of the forward")
     ap.add_argument("--secondary", action="store_true",
                     help="also time the 16K non-causal forward (the other "
                          "shape the metric names); off by default so that a "
@@ -195,6 +294,9 @@ def main():
 
     w = inputs.CONFIGS[args.workload]
     causal = bool(args.causal)
+    if args.backward:
+        main_backward(args, w, causal)
+        return
     r = time_forward(w, causal, args.steps, args.warmup)
     tflops = r["flops"] / (r["wall_ms"] * 1e-3) / 1e12
     k_tflops = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
@@ -250,6 +352,54 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle on a row sample) ...")
         out["cpu_baseline"] = cpu_baseline(w, causal, r)
+        log(f"bench: cpu baseline {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+
+
+def main_backward(args, w, causal):
+    steps = args.steps if args.steps != 200 else 40
+    warmup = args.warmup if args.warmup != 50 else 10
+    r = time_backward(w, causal, steps, warmup)
+    tflops = r["flops"] / (r["wall_ms"] * 1e-3) / 1e12
+    k_tflops = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+    log(f"bench: backward wall {r['wall_ms']:.4f} ms/step, kernels "
+        f"{r['kernel_ms']:.4f} ms/call, {k_tflops:.1f} TFLOP/s")
+    out = {
+        "metric": "attention bwd TFLOP/s (algorithmic 2.5x forward flops) and % "
+                  "of bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(r["wall_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else w.dtype,
+        "data": "synthetic",
+        "config": {"workload": workload_desc(w, causal) + " backward", "B": w.B,
+                   "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "D": w.D, "causal": causal,
+                   "scale": w.scale, "io_dtype": w.dtype, "kernel": r["kernel"]},
+        "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(k_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "fa_bwd call: delta, " + r["kernel"] + " (dK/dV), dQ",
+            "flops_per_launch": r["flops"],
+            "kernel_ms": round(r["kernel_ms"], 5),
+        },
+    }
+    log("bench: backward parity (one head vs oracle) ...")
+    out["parity"] = parity_bwd(w, causal, r)
+    log(f"bench: parity {out['parity']}")
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle backward on whole heads) ...")
+        out["cpu_baseline"] = cpu_baseline_bwd(w, causal, r)
         log(f"bench: cpu baseline {out['cpu_baseline']}")
     print(json.dumps(out), flush=True)
 

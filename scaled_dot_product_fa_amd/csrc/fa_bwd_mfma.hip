@@ -39,6 +39,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -52,6 +54,25 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+#ifndef BWD_KV_OCC64
+#define BWD_KV_OCC64 2
+#endif
+#ifndef BWD_KV_OCC128
+#define BWD_KV_OCC128 1
+#endif
+#ifndef BWD_KV_SCHED
+#define BWD_KV_SCHED 1
+#endif
+#ifndef BWD_KV_VPER
+#define BWD_KV_VPER 10
+#endif
+#ifndef BWD_Q_OCC64
+#define BWD_Q_OCC64 2
+#endif
+#ifndef BWD_Q_OCC128
+#define BWD_Q_OCC128 2
+#endif
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;   // 4 waves per workgroup
@@ -121,6 +142,38 @@ __device__ __forceinline__ uint2 ds_read_tr(const uint8_t *p)
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// global_load_lds_dwordx4 / _dword: every lane fetches 16 (4) bytes from its
+// own global address and the hardware writes them to LDS at m0 + 16 (4) *
+// lane.  Issued from inline assembly so that the compiler does not count
+// them: it would otherwise wait for every outstanding LDS read before each
+// use of any of them.  The kernels order them with explicit vmcnt waits and
+// barriers, and drain them before exit.
+__device__ __forceinline__ void dma_16B(const void *src, uint32_t lds_dst)
+{
+    __asm__ volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_dst) : "memory");
+}
+
+__device__ __forceinline__ void dma_4B(const void *src, uint32_t lds_dst)
+{
+    __asm__ volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_dst) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
 
 struct BwdParams {
     const uint16_t *q, *k, *v, *dout;
@@ -197,25 +250,35 @@ __device__ __forceinline__ void store_cols(uint16_t *row_base, int db, int hi, c
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per 128 keys, 32 per wave; query tiles of 32 rows.
+// dK, dV: one workgroup per 128 keys, 32 per wave; query tiles of 32 rows,
+// software-pipelined: in step t the S and dP products of tile t+1 and the
+// dV, dK products of tile t are issued together, and the probabilities of
+// tile t+1 are computed while the latter run.  Tiles reach LDS by direct
+// loads (Q and dO rows, the 32 lse and 32 delta values) into four rotating
+// buffers: tile t+3 is requested in step t and needed at the end of step
+// t+1.  One barrier per step.  Causal tiles a wave cannot see are computed
+// and masked to zero (no branch inside a step).
 // ---------------------------------------------------------------------------
-template <typename Ops, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <typename Ops, int D, bool CAUSAL, int OCC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_bwd_dkdv_mfma_kernel(BwdParams p)
 {
     constexpr int NW = kThreads / 64;
-    constexpr int BK = NW * 32;          // keys per workgroup
-    constexpr int BQ = 32;               // query rows per tile
+    constexpr int BK = NW * 32;
+    constexpr int BQ = 32;
     constexpr int DC = D / 16, DB = D / 32;
     constexpr int ROWB = D * 2;
-    constexpr int CH = D / 8;            // 16-byte chunks per row
+    constexpr int CH = D / 8;
     constexpr int TILEB = BQ * ROWB;
-    constexpr int NLD = BQ * CH / kThreads;   // chunks per thread per tensor
+    constexpr int NLD = BQ * CH / kThreads;     // 16-byte loads per lane per tensor
+    constexpr int LPI = 2 * NLD + 1;            // loads per lane per tile
     constexpr int BUFB = 2 * TILEB + 2 * BQ * 4;
+    constexpr int NBUF = 4;
     static_assert(NLD >= 1 && BQ * CH % kThreads == 0, "tile split");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUFB];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * BUFB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
     int bh, kt;
     decompose(blockIdx.x, gridDim.x, p.BH, p.nt, CAUSAL, true, bh, kt);
@@ -226,10 +289,9 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
 
     const uint16_t *qh = p.q + (int64_t)bh * Lq * D;
     const uint16_t *gh = p.dout + (int64_t)bh * Lq * D;
-    const float *lh = p.lse + (int64_t)bh * Lq;
-    const float *dh = p.delta + (int64_t)bh * Lq;
+    // lane l < 32 loads lse of row l of a tile, lane l >= 32 delta of row l-32
+    const float *xh = (lane < 32 ? p.lse : p.delta) + (int64_t)bh * Lq;
 
-    // K and V rows of this lane's key: B operands of S = Q K^T, dP = dO V^T
     u32x4 kop[DC], vop[DC];
     {
         const uint16_t *kr = p.k + ((int64_t)bh * Lk + key) * D + 8 * hi;
@@ -249,18 +311,32 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
             dv[db][i] = 0.f;
         }
 
-    // staging: thread -> (row, chunk) pairs of a tile
-    int st_row[NLD];
-    uint32_t st_g[NLD], st_l[NLD];
+    // Direct loads: load n of a wave fills the 1 KB at LDS chunk position
+    // (n*NW + wave)*64 + lane of a tile; that position is row pos / CH,
+    // physical chunk pos % CH, which holds logical chunk phys ^ swz(row).
+    int dm_row[NLD];
+    uint32_t dm_col[NLD];
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-        const int idx = tid + n * kThreads;
-        const int row = idx / CH, pc = idx % CH;
-        st_row[n] = row;
-        st_g[n] = (uint32_t)(row * D + pc * 8);
-        st_l[n] = (uint32_t)(row * ROWB + ((pc ^ swz<D>(row)) * 16));
+        const int pos = (n * NW + wave) * 64 + lane;
+        const int row = pos / CH, phys = pos % CH;
+        dm_row[n] = row;
+        dm_col[n] = (uint32_t)(((phys ^ swz<D>(row)) * 8));
     }
-    // permuted row reads (A of S and dP) and transposing reads (A of dV^T, dK^T)
+    const uint32_t smem_base = lds_addr(smem);
+    // Rows past the end fetch the last row (valid memory); the probabilities
+    // of those rows are masked to zero in the last step.
+    auto issue = [&](int i0, uint32_t b) {
+        const uint32_t wb = uniform(smem_base + b + (uint32_t)(wave * 1024));
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) {
+            const int64_t o = (int64_t)min(i0 + dm_row[n], Lq - 1) * D + dm_col[n];
+            dma_16B(qh + o, wb + (uint32_t)(n * NW * 1024));
+            dma_16B(gh + o, wb + TILEB + (uint32_t)(n * NW * 1024));
+        }
+        dma_4B(xh + min(i0 + l32, Lq - 1), uniform(smem_base + b + 2 * TILEB));
+    };
+
     uint32_t rd_row[DC];
     {
         const int row = swap_bits23(l32);
@@ -271,93 +347,129 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
     uint32_t rd_tr[DB][2];
     tr_offsets<D, DB>(lane, rd_tr);
 
-    const int i_begin = CAUSAL ? k_first : 0;   // rows above the block see none of its keys
+    const int i_begin = CAUSAL ? k_first : 0;
     const int ntiles = i_begin < Lq ? (Lq - i_begin + BQ - 1) / BQ : 0;
 
-    u32x4 stq[NLD], stg[NLD];
-    float st_x = 0.f;
-    auto fetch = [&](int i0) {
+    f32x16 s, dp;
+    u32x4 pk[2], dsk[2];
+    auto sdp = [&](uint32_t b) {
+        u32x4 aq[DC], ag[DC];
 #pragma unroll
-        for (int n = 0; n < NLD; ++n) {
-            const bool ok = i0 + st_row[n] < Lq;
-            const int64_t o = (int64_t)i0 * D + st_g[n];
-            stq[n] = ok ? *(const u32x4 *)(qh + o) : u32x4{0u, 0u, 0u, 0u};
-            stg[n] = ok ? *(const u32x4 *)(gh + o) : u32x4{0u, 0u, 0u, 0u};
+        for (int dc = 0; dc < DC; ++dc) {
+            aq[dc] = *(const u32x4 *)(smem + b + rd_row[dc]);
+            ag[dc] = *(const u32x4 *)(smem + b + TILEB + rd_row[dc]);
         }
-        if (tid < 2 * BQ) {
-            const int i = i0 + (tid & (BQ - 1));
-            // rows past the end: lse = +inf makes their probabilities 0
-            if (tid < BQ) st_x = i < Lq ? lh[i] * kLog2e : INFINITY;
-            else st_x = i < Lq ? dh[i] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s[i] = 0.f;
+            dp[i] = 0.f;
+        }
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+            s = Ops::mma(aq[dc], kop[dc], s);
+            dp = Ops::mma(ag[dc], vop[dc], dp);
         }
     };
-    auto stage = [&](uint8_t *buf) {
+    // Probabilities and ds of the tile at rows i0.. (in LDS at b).  TAIL:
+    // also zero the rows past the end of the queries.
+    auto probs = [&](uint32_t b, int i0, auto tail) {
+        // lse and delta of rows 8*hi + 0..7 and 16 + 8*hi + 0..7
+        const float4 *lt4 = (const float4 *)(smem + b + 2 * TILEB) + 2 * hi;
+        const float4 *dl4 = lt4 + BQ / 4;
+        float L[16], Dl[16];
 #pragma unroll
-        for (int n = 0; n < NLD; ++n) {
-            *(u32x4 *)(buf + st_l[n]) = stq[n];
-            *(u32x4 *)(buf + TILEB + st_l[n]) = stg[n];
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int src = (q4 & 1) + 4 * (q4 >> 1);
+            const float4 a = lt4[src], d = dl4[src];
+            L[4 * q4] = a.x; L[4 * q4 + 1] = a.y; L[4 * q4 + 2] = a.z; L[4 * q4 + 3] = a.w;
+            Dl[4 * q4] = d.x; Dl[4 * q4 + 1] = d.y; Dl[4 * q4 + 2] = d.z; Dl[4 * q4 + 3] = d.w;
         }
-        if (tid < 2 * BQ) ((float *)(buf + 2 * TILEB))[tid] = st_x;
+        // causal: keep key kw + l32 for row i0 + row when row >= lim
+        const int lim = (CAUSAL && i0 < kw + 31) ? kw + l32 - i0 : -1;
+        const int rows = Lq - i0;
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float e = exp2_fast(fmaf(s[r], p.c, -L[r] * kLog2e));
+            if (CAUSAL) e = acc_row(r, hi) >= lim ? e : 0.f;
+            if (decltype(tail)::value) e = acc_row(r, hi) < rows ? e : 0.f;
+            pv[r] = e;
+            dsv[r] = e * (dp[r] - Dl[r]);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                pk[h][w] = Ops::pack2(pv[8 * h + 2 * w], pv[8 * h + 2 * w + 1]);
+                dsk[h][w] = Ops::pack2(dsv[8 * h + 2 * w], dsv[8 * h + 2 * w + 1]);
+            }
+    };
+    auto grads = [&](uint32_t b) {
+        u32x4 tg[2][DB], tq[2][DB];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            const uint32_t co = (uint32_t)(kc * 16 * ROWB);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                tg[kc][db] = read_tr<DB>(smem + b + TILEB, rd_tr, db, co);
+                tq[kc][db] = read_tr<DB>(smem + b, rd_tr, db, co);
+            }
+        }
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                dv[db] = Ops::mma(tg[kc][db], pk[kc], dv[db]);
+                dk[db] = Ops::mma(tq[kc][db], dsk[kc], dk[db]);
+            }
+    };
+    auto buf = [&](int t) { return (uint32_t)((t & (NBUF - 1)) * BUFB); };
+    using no_tail = std::integral_constant<bool, false>;
+    using with_tail = std::integral_constant<bool, true>;
+
+    // One step: tile t+3 requested, S/dP of tile t+1, dV/dK of tile t, the
+    // probabilities of tile t+1; then tile t+2 must have arrived.
+    auto step = [&](int t, auto tail) {
+        const int i0 = i_begin + t * BQ;
+        issue(i0 + 3 * BQ, buf(t + 3));
+        sdp(buf(t + 1));
+        grads(buf(t));
+        probs(buf(t + 1), i0 + BQ, tail);
+#if BWD_KV_SCHED
+        // the loads first; the S/dP operands; the S/dP products with the
+        // transposing reads of the dV/dK operands between them; the dV/dK
+        // products with the probabilities of tile t+1 between them
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DC, 0);        // DS read
+#pragma unroll
+        for (int n = 0; n < 2 * DC; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB / DC + 1, 0);
+        }
+#pragma unroll
+        for (int n = 0; n < 4 * DB; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (n >= 2) __builtin_amdgcn_sched_group_barrier(0x002, BWD_KV_VPER, 0);  // VALU
+        }
+#endif
+        wait_vmcnt<LPI>();
+        __syncthreads();
     };
 
     if (ntiles > 0) {
-        fetch(i_begin);
-        stage(smem);
+        // tiles 0, 1, 2 (past the end: clamped rows, never used)
+        issue(i_begin, buf(0));
+        issue(i_begin + BQ, buf(1));
+        issue(i_begin + 2 * BQ, buf(2));
+        wait_vmcnt<LPI>();
         __syncthreads();
+        sdp(buf(0));
+        probs(buf(0), i_begin, with_tail());
+        int t = 0;
+        for (; t + 2 < ntiles; ++t) step(t, no_tail());
+        if (t + 1 < ntiles) step(t++, with_tail());
+        grads(buf(t));
     }
-    for (int t = 0; t < ntiles; ++t) {
-        const int i0 = i_begin + t * BQ;
-        const uint8_t *cur = smem + (t & 1) * BUFB;
-        uint8_t *nxt = smem + ((t + 1) & 1) * BUFB;
-        const bool more = t + 1 < ntiles;
-        if (more) fetch(i0 + BQ);
-        // causal: this wave's keys are invisible to the whole tile when
-        // i0 + 31 < kw; the tile needs a mask only on the diagonal (i0 == kw)
-        if (!CAUSAL || i0 + BQ - 1 >= kw) {
-            const uint8_t *qt = cur, *gt = cur + TILEB;
-            const float *lt = (const float *)(cur + 2 * TILEB), *dlt = lt + BQ;
-            f32x16 s, dp;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s[i] = 0.f;
-                dp[i] = 0.f;
-            }
-#pragma unroll
-            for (int dc = 0; dc < DC; ++dc) {
-                s = Ops::mma(*(const u32x4 *)(qt + rd_row[dc]), kop[dc], s);
-                dp = Ops::mma(*(const u32x4 *)(gt + rd_row[dc]), vop[dc], dp);
-            }
-            float pv[16], dsv[16];
-            const bool diag = CAUSAL && i0 == kw;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = acc_row(r, hi);
-                float e = exp2_fast(fmaf(s[r], p.c, -lt[row]));
-                if (diag) e = l32 <= row ? e : 0.f;
-                pv[r] = e;
-                dsv[r] = e * (dp[r] - dlt[row]);
-            }
-            u32x4 pk[2], dsk[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    pk[h][w] = Ops::pack2(pv[8 * h + 2 * w], pv[8 * h + 2 * w + 1]);
-                    dsk[h][w] = Ops::pack2(dsv[8 * h + 2 * w], dsv[8 * h + 2 * w + 1]);
-                }
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const uint32_t co = (uint32_t)(kc * 16 * ROWB);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    dv[db] = Ops::mma(read_tr<DB>(gt, rd_tr, db, co), pk[kc], dv[db]);
-                    dk[db] = Ops::mma(read_tr<DB>(qt, rd_tr, db, co), dsk[kc], dk[db]);
-                }
-            }
-        }
-        if (more) stage(nxt);
-        __syncthreads();
-    }
+    wait_vmcnt<0>();
 
     if (key < Lk) {
         uint16_t *dkr = p.dk + ((int64_t)bh * Lk + key) * D;
@@ -373,8 +485,8 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per 128 query rows, 32 per wave; key tiles of 64.
 // ---------------------------------------------------------------------------
-template <typename Ops, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <typename Ops, int D, bool CAUSAL, int OCC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_bwd_dq_mfma_kernel(BwdParams p)
 {
     constexpr int NW = kThreads / 64;
@@ -390,7 +502,8 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
     static_assert(NLD >= 1 && BN * CH % kThreads == 0, "tile split");
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUFB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
     int bh, qt;
     decompose(blockIdx.x, gridDim.x, p.BH, p.nt, CAUSAL, false, bh, qt);
@@ -422,16 +535,18 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
 #pragma unroll
         for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
 
-    int st_row[NLD];
-    uint32_t st_g[NLD], st_l[NLD];
+    // Direct loads, as in the dK/dV kernel: load n of a wave fills LDS chunk
+    // positions (n*NW + wave)*64 + lane of a tile.
+    int dm_row[NLD];
+    uint32_t dm_col[NLD];
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-        const int idx = tid + n * kThreads;
-        const int row = idx / CH, pc = idx % CH;
-        st_row[n] = row;
-        st_g[n] = (uint32_t)(row * D + pc * 8);
-        st_l[n] = (uint32_t)(row * ROWB + ((pc ^ swz<D>(row)) * 16));
+        const int pos = (n * NW + wave) * 64 + lane;
+        const int row = pos / CH, phys = pos % CH;
+        dm_row[n] = row;
+        dm_col[n] = (uint32_t)(((phys ^ swz<D>(row)) * 8));
     }
+    const uint32_t smem_base = lds_addr(smem);
     uint32_t rd_row[DC];
     {
         const int row = swap_bits23(l32);
@@ -445,35 +560,28 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
     const int kv_end = CAUSAL ? min(Lk, q_first + BM) : Lk;
     const int ntiles = (kv_end + BN - 1) / BN;
 
-    u32x4 stk[NLD], stv[NLD];
-    auto fetch = [&](int k0) {
+    // Keys past the end fetch the last key (valid memory); their
+    // probabilities are masked to zero.
+    auto issue = [&](int k0, uint32_t b) {
+        const uint32_t wb = uniform(smem_base + b + (uint32_t)(wave * 1024));
 #pragma unroll
         for (int n = 0; n < NLD; ++n) {
-            const bool ok = k0 + st_row[n] < Lk;
-            const int64_t o = (int64_t)k0 * D + st_g[n];
-            stk[n] = ok ? *(const u32x4 *)(kh + o) : u32x4{0u, 0u, 0u, 0u};
-            stv[n] = ok ? *(const u32x4 *)(vh + o) : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto stage = [&](uint8_t *buf) {
-#pragma unroll
-        for (int n = 0; n < NLD; ++n) {
-            *(u32x4 *)(buf + st_l[n]) = stk[n];
-            *(u32x4 *)(buf + TILEB + st_l[n]) = stv[n];
+            const int64_t o = (int64_t)min(k0 + dm_row[n], Lk - 1) * D + dm_col[n];
+            dma_16B(kh + o, wb + (uint32_t)(n * NW * 1024));
+            dma_16B(vh + o, wb + TILEB + (uint32_t)(n * NW * 1024));
         }
     };
 
     if (ntiles > 0) {
-        fetch(0);
-        stage(smem);
+        issue(0, 0);
+        wait_vmcnt<0>();
         __syncthreads();
     }
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * BN;
         const uint8_t *cur = smem + (t & 1) * BUFB;
-        uint8_t *nxt = smem + ((t + 1) & 1) * BUFB;
         const bool more = t + 1 < ntiles;
-        if (more) fetch(k0 + BN);
+        if (more) issue(k0 + BN, (uint32_t)(((t + 1) & 1) * BUFB));
         if (!CAUSAL || k0 <= qw + 31) {
             const uint8_t *kt = cur, *vt = cur + TILEB;
             // mask: keys past the diagonal (causal) or past the end
@@ -518,7 +626,7 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
                     dq[db] = Ops::mma(read_tr<DB>(kt, rd_tr, db, co), dsk[kc], dq[db]);
             }
         }
-        if (more) stage(nxt);
+        wait_vmcnt<0>();
         __syncthreads();
     }
 
@@ -549,12 +657,12 @@ hipError_t launch_t(const BwdArgs &a)
     p.c = a.scale * kLog2e;
     constexpr int BLK = (kThreads / 64) * 32;
     p.nt = (int)((a.Lk + BLK - 1) / BLK);
-    hipLaunchKernelGGL((fa_bwd_dkdv_mfma_kernel<Ops, D, CAUSAL>),
+    hipLaunchKernelGGL((fa_bwd_dkdv_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_KV_OCC64 : BWD_KV_OCC128>),
                        dim3((unsigned)(p.BH * p.nt)), dim3(kThreads), 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     p.nt = (int)((a.Lq + BLK - 1) / BLK);
-    hipLaunchKernelGGL((fa_bwd_dq_mfma_kernel<Ops, D, CAUSAL>),
+    hipLaunchKernelGGL((fa_bwd_dq_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_Q_OCC64 : BWD_Q_OCC128>),
                        dim3((unsigned)(p.BH * p.nt)), dim3(kThreads), 0, a.stream, p);
     return hipGetLastError();
 }
