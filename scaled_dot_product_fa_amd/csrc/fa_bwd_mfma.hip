@@ -15,8 +15,8 @@
 //
 //   * dK/dV kernel, one workgroup per block of keys.  Each wave owns 32 keys
 //     and keeps their K and V rows in VGPRs as MFMA B operands.  Tiles of 32
-//     query rows of Q and dO stream through LDS (double-buffered, staged
-//     through VGPRs).  Per tile: S = Q K^T and dP = dO V^T on
+//     query rows of Q and dO stream through LDS (direct global-to-LDS loads,
+//     four buffers, software-pipelined).  Per tile: S = Q K^T and dP = dO V^T on
 //     v_mfma_f32_32x32x16_{bf16,f16} with the Q/dO rows read in a permuted
 //     order (bits 2 and 3 of the row swapped), so each lane's accumulator
 //     holds one key column and two runs of 8 consecutive queries.  P and dS,
@@ -25,15 +25,24 @@
 //     tiles through ds_read_b64_tr_b16 (transposing reads).
 //   * dQ kernel, one workgroup per block of query rows, the forward's layout:
 //     each wave owns 32 queries with Q^T and dO^T in VGPRs; tiles of 64 keys
-//     of K and V stream through LDS; S^T = K Q^T and dP^T = V dO^T put one
-//     query column in each lane; dS^T is the B operand of dQ^T += K^T dS^T,
-//     K^T read from the K tile with transposing reads.
+//     of K and V stream through LDS (direct loads, two buffers); S^T = K Q^T
+//     and dP^T = V dO^T put one query column in each lane; dS^T is the B
+//     operand of dQ^T += K^T dS^T, K^T read from the K tile with transposing
+//     reads.
 //
 // The LDS tiles are row-major with 16-byte chunks XOR-swizzled by row with a
 // pattern that keeps both the permuted row reads and the transposing reads
 // free of bank conflicts.  exp uses exp2 with scale*log2(e) folded into one
-// FMA.  Causal tiles that a wave cannot see are skipped; only tiles on the
-// diagonal are masked (key j kept for query i when j <= i).
+// FMA.  Causal masking keeps key j for query i when j <= i: the dQ kernel
+// skips key tiles a wave cannot see and masks only tiles that cross the
+// diagonal; the dK/dV kernel starts at the first query tile that can see its
+// keys and masks (rather than branches around) the few tiles a wave cannot
+// see, so each pipeline step stays one straight-line block.
+//
+// Compile-time knobs (defaults are the measured best): waves per SIMD each
+// kernel is register-budgeted for, at D = 64 and D = 128 (BWD_*_OCC*), and
+// whether the dK/dV step pins its MFMA / LDS-read / VALU interleave with
+// sched_group_barrier (BWD_KV_SCHED; BWD_KV_VPER VALU ops per slot).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
