@@ -51,6 +51,16 @@ def _bind(lib):
                                           _I64, _I64, ctypes.c_int,
                                           ctypes.c_double]
     lib.oracle_attention_rows.restype = ctypes.c_int
+    lib.oracle_attention_win.argtypes = [_F64P, _F64P, _F64P, _F64P, _F64P,
+                                         _I64, _I64, _I64, _I64, _I64,
+                                         ctypes.c_int, _I64, _I64,
+                                         ctypes.c_double]
+    lib.oracle_attention_win.restype = ctypes.c_int
+    lib.oracle_attention_rows_win.argtypes = [_F64P, _F64P, _F64P, _I64P, _I64,
+                                              _F64P, _F64P, _I64, _I64, _I64,
+                                              _I64, _I64, ctypes.c_int, _I64,
+                                              _I64, ctypes.c_double]
+    lib.oracle_attention_rows_win.restype = ctypes.c_int
     lib.oracle_probs.argtypes = [_F64P, _F64P, _F64P, _I64, _I64, _I64, _I64,
                                  _I64, ctypes.c_int, ctypes.c_double]
     lib.oracle_probs.restype = ctypes.c_int
@@ -94,28 +104,38 @@ def _shapes(q, k, v):
 
 
 def attention(q, k, v, causal: bool = False, scale: float | None = None,
-              lib=None):
-    """Full fp64 forward.  Returns (o [B,H,Lq,D], lse [B,H,Lq])."""
+              lib=None, window=None):
+    """Full fp64 forward.  Returns (o [B,H,Lq,D], lse [B,H,Lq]).
+
+    ``window=(wl, wr)`` keeps key j for query i only when i - wl <= j <= i + wr
+    (a negative bound is no bound)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, Lq, Lk, D = _shapes(q, k, v)
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     o = np.empty((B, H, Lq, D), dtype=np.float64)
     lse = np.empty((B, H, Lq), dtype=np.float64)
-    rc = (lib or load()).oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                          _ptr(lse), B, H, Lq, Lk, D,
-                                          int(bool(causal)), float(scale))
+    lib = lib or load()
+    if window is None:
+        rc = lib.oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(lse), B, H, Lq, Lk, D,
+                                  int(bool(causal)), float(scale))
+    else:
+        rc = lib.oracle_attention_win(_ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                      _ptr(lse), B, H, Lq, Lk, D,
+                                      int(bool(causal)), int(window[0]),
+                                      int(window[1]), float(scale))
     if rc != 0:
         raise RuntimeError(f"oracle_attention failed ({rc})")
     return o, lse
 
 
 def attention_rows(q, k, v, row_ids, causal: bool = False,
-                   scale: float | None = None, lib=None):
+                   scale: float | None = None, lib=None, window=None):
     """Selected rows.  row_ids are flat (b*H + h)*Lq + i indices.
 
     Returns (o_rows [n, D], lse_rows [n]); each row equals the matching row of
-    :func:`attention`.
+    :func:`attention` (same ``window`` convention).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, Lq, Lk, D = _shapes(q, k, v)
@@ -125,9 +145,10 @@ def attention_rows(q, k, v, row_ids, causal: bool = False,
     n = ids.size
     o = np.empty((n, D), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
-    rc = (lib or load()).oracle_attention_rows(
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    rc = (lib or load()).oracle_attention_rows_win(
         _ptr(q), _ptr(k), _ptr(v), ids.ctypes.data_as(_I64P), n, _ptr(o),
-        _ptr(lse), B, H, Lq, Lk, D, int(bool(causal)), float(scale))
+        _ptr(lse), B, H, Lq, Lk, D, int(bool(causal)), wl, wr, float(scale))
     if rc != 0:
         raise RuntimeError(f"oracle_attention_rows failed ({rc})")
     return o, lse

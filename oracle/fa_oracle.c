@@ -20,6 +20,11 @@
  * j <= i (the diagonal is kept), indices counted from the top-left corner.
  * Keys j >= Lk do not exist and are never visited.
  *
+ * Local (sliding-window) masking, one of the mask variants the article
+ * leaves for later: with window_left wl >= 0 query i also drops keys
+ * j < i - wl, with window_right wr >= 0 it drops keys j > i + wr; a negative
+ * bound means no bound.  Causal and a window combine (both must keep j).
+ *
  * For every row (b, h, i):
  *   J    = { 0 <= j < Lk : (!causal) or j <= i }
  *   s_j  = scale * sum_d q[b,h,i,d] * k[b,h,j,d]          (j in J)
@@ -43,11 +48,19 @@
 #include <omp.h>
 #endif
 
-/* One past the last visible key of query row i. */
-static int64_t visible_end(int64_t i, int64_t Lk, int causal)
+/* Visible keys of query row i: [visible_begin, visible_end). */
+static int64_t visible_end(int64_t i, int64_t Lk, int causal, int64_t wr)
 {
-    if (!causal) return Lk;
-    return (i + 1 < Lk) ? i + 1 : Lk;
+    int64_t e = Lk;
+    if (causal && i + 1 < e) e = i + 1;
+    if (wr >= 0 && i + wr + 1 < e) e = i + wr + 1;
+    return e;
+}
+
+static int64_t visible_begin(int64_t i, int64_t wl)
+{
+    if (wl < 0 || i - wl <= 0) return 0;
+    return i - wl;
 }
 
 /*
@@ -56,20 +69,20 @@ static int64_t visible_end(int64_t i, int64_t Lk, int causal)
  * Returns 0 when the row has no visible key (then p is all zero).
  */
 static int softmax_row(const double *q_row, const double *k_head, int64_t Lk,
-                       int64_t D, int64_t jend, double scale, double *p,
-                       double *m_out, double *l_out)
+                       int64_t D, int64_t jbeg, int64_t jend, double scale,
+                       double *p, double *m_out, double *l_out)
 {
     int64_t j, d;
     double m = -INFINITY, l = 0.0;
 
     for (j = 0; j < Lk; ++j) p[j] = 0.0;
-    if (jend <= 0) {
+    if (jend <= jbeg) {
         *m_out = -INFINITY;
         *l_out = 0.0;
         return 0;
     }
     /* scores, and pass 1: the row maximum */
-    for (j = 0; j < jend; ++j) {
+    for (j = jbeg; j < jend; ++j) {
         const double *k_row = k_head + j * D;
         double dot = 0.0;
         for (d = 0; d < D; ++d) dot += q_row[d] * k_row[d];
@@ -77,23 +90,23 @@ static int softmax_row(const double *q_row, const double *k_head, int64_t Lk,
         if (p[j] > m) m = p[j];
     }
     /* pass 2: exponentials relative to the maximum, and their sum */
-    for (j = 0; j < jend; ++j) {
+    for (j = jbeg; j < jend; ++j) {
         p[j] = exp(p[j] - m);
         l += p[j];
     }
-    for (j = 0; j < jend; ++j) p[j] /= l;
+    for (j = jbeg; j < jend; ++j) p[j] /= l;
     *m_out = m;
     *l_out = l;
     return 1;
 }
 
 /* o_row[d] = sum_j p[j] * v[b,h,j,d] over the visible keys. */
-static void weighted_sum(const double *p, const double *v_head, int64_t jend,
-                         int64_t D, double *o_row)
+static void weighted_sum(const double *p, const double *v_head, int64_t jbeg,
+                         int64_t jend, int64_t D, double *o_row)
 {
     int64_t j, d;
     for (d = 0; d < D; ++d) o_row[d] = 0.0;
-    for (j = 0; j < jend; ++j) {
+    for (j = jbeg; j < jend; ++j) {
         const double *v_row = v_head + j * D;
         for (d = 0; d < D; ++d) o_row[d] += p[j] * v_row[d];
     }
@@ -107,33 +120,34 @@ static int check_shape(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D)
 /* One row (b*H + h, i) of the output: o_row[0..D) and *lse_out. */
 static void one_row(const double *q, const double *k, const double *v,
                     int64_t bh, int64_t i, int64_t Lq, int64_t Lk, int64_t D,
-                    int causal, double scale, double *p, double *o_row,
-                    double *lse_out)
+                    int causal, int64_t wl, int64_t wr, double scale, double *p,
+                    double *o_row, double *lse_out)
 {
     const double *q_row = q + (bh * Lq + i) * D;
     const double *k_head = k + bh * Lk * D;
     const double *v_head = v + bh * Lk * D;
-    int64_t jend = visible_end(i, Lk, causal);
+    int64_t jbeg = visible_begin(i, wl), jend = visible_end(i, Lk, causal, wr);
     double m, l;
 
-    if (!softmax_row(q_row, k_head, Lk, D, jend, scale, p, &m, &l)) {
+    if (!softmax_row(q_row, k_head, Lk, D, jbeg, jend, scale, p, &m, &l)) {
         int64_t d;
         for (d = 0; d < D; ++d) o_row[d] = 0.0;
         *lse_out = -INFINITY;
         return;
     }
-    weighted_sum(p, v_head, jend, D, o_row);
+    weighted_sum(p, v_head, jbeg, jend, D, o_row);
     *lse_out = m + log(l);
 }
 
 /*
  * Full forward: q [B,H,Lq,D], k and v [B,H,Lk,D], o [B,H,Lq,D], lse [B,H,Lq],
- * all contiguous row-major fp64.  Returns 0, or -1 on a bad shape or an
- * allocation failure.
+ * all contiguous row-major fp64; wl / wr are the window bounds (negative: no
+ * bound).  Returns 0, or -1 on a bad shape or an allocation failure.
  */
-int oracle_attention(const double *q, const double *k, const double *v,
-                     double *o, double *lse, int64_t B, int64_t H, int64_t Lq,
-                     int64_t Lk, int64_t D, int causal, double scale)
+int oracle_attention_win(const double *q, const double *k, const double *v,
+                         double *o, double *lse, int64_t B, int64_t H,
+                         int64_t Lq, int64_t Lk, int64_t D, int causal,
+                         int64_t wl, int64_t wr, double scale)
 {
     int64_t rows = B * H * Lq, r;
     int failed = 0;
@@ -148,7 +162,7 @@ int oracle_attention(const double *q, const double *k, const double *v,
 #pragma omp for schedule(dynamic, 16)
             for (r = 0; r < rows; ++r) {
                 int64_t bh = r / Lq, i = r % Lq;
-                one_row(q, k, v, bh, i, Lq, Lk, D, causal, scale, p,
+                one_row(q, k, v, bh, i, Lq, Lk, D, causal, wl, wr, scale, p,
                         o + r * D, lse + r);
             }
         }
@@ -157,16 +171,26 @@ int oracle_attention(const double *q, const double *k, const double *v,
     return failed ? -1 : 0;
 }
 
+/* The forward without a window. */
+int oracle_attention(const double *q, const double *k, const double *v,
+                     double *o, double *lse, int64_t B, int64_t H, int64_t Lq,
+                     int64_t Lk, int64_t D, int causal, double scale)
+{
+    return oracle_attention_win(q, k, v, o, lse, B, H, Lq, Lk, D, causal, -1,
+                                -1, scale);
+}
+
 /*
  * Selected rows only.  row_ids[n] = (b*H + h)*Lq + i names a query row; the
  * outputs are packed: o_rows [nrows, D], lse_rows [nrows].  Rows are
  * independent, so each selected row is exactly what oracle_attention gives.
  */
-int oracle_attention_rows(const double *q, const double *k, const double *v,
-                          const int64_t *row_ids, int64_t nrows,
-                          double *o_rows, double *lse_rows, int64_t B,
-                          int64_t H, int64_t Lq, int64_t Lk, int64_t D,
-                          int causal, double scale)
+int oracle_attention_rows_win(const double *q, const double *k,
+                              const double *v, const int64_t *row_ids,
+                              int64_t nrows, double *o_rows, double *lse_rows,
+                              int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                              int64_t D, int causal, int64_t wl, int64_t wr,
+                              double scale)
 {
     int64_t n;
     int failed = 0;
@@ -183,13 +207,24 @@ int oracle_attention_rows(const double *q, const double *k, const double *v,
 #pragma omp for schedule(dynamic, 4)
             for (n = 0; n < nrows; ++n) {
                 int64_t r = row_ids[n];
-                one_row(q, k, v, r / Lq, r % Lq, Lq, Lk, D, causal, scale, p,
-                        o_rows + n * D, lse_rows + n);
+                one_row(q, k, v, r / Lq, r % Lq, Lq, Lk, D, causal, wl, wr,
+                        scale, p, o_rows + n * D, lse_rows + n);
             }
         }
         free(p);
     }
     return failed ? -1 : 0;
+}
+
+int oracle_attention_rows(const double *q, const double *k, const double *v,
+                          const int64_t *row_ids, int64_t nrows,
+                          double *o_rows, double *lse_rows, int64_t B,
+                          int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                          int causal, double scale)
+{
+    return oracle_attention_rows_win(q, k, v, row_ids, nrows, o_rows,
+                                     lse_rows, B, H, Lq, Lk, D, causal, -1, -1,
+                                     scale);
 }
 
 /*
@@ -206,8 +241,9 @@ int oracle_probs(const double *q, const double *k, double *p_out, int64_t B,
     for (r = 0; r < rows; ++r) {
         int64_t bh = r / Lq, i = r % Lq;
         double m, l;
-        softmax_row(q + r * D, k + bh * Lk * D, Lk, D, visible_end(i, Lk, causal),
-                    scale, p_out + r * Lk, &m, &l);
+        softmax_row(q + r * D, k + bh * Lk * D, Lk, D, 0,
+                    visible_end(i, Lk, causal, -1), scale, p_out + r * Lk, &m,
+                    &l);
     }
     return 0;
 }
@@ -262,9 +298,9 @@ int oracle_attention_bwd(const double *q, const double *k, const double *v,
         for (i = 0; i < Lq; ++i) {
             double *pi = p + i * Lk, *dsi = ds + i * Lk;
             const double *gi = gh + i * D;
-            int64_t jend = visible_end(i, Lk, causal), jj, d;
+            int64_t jend = visible_end(i, Lk, causal, -1), jj, d;
             double m, l, delta = 0.0;
-            softmax_row(qh + i * D, kh, Lk, D, jend, scale, pi, &m, &l);
+            softmax_row(qh + i * D, kh, Lk, D, 0, jend, scale, pi, &m, &l);
             for (jj = 0; jj < Lk; ++jj) dsi[jj] = 0.0;
             for (jj = 0; jj < jend; ++jj) {
                 const double *vj = vh + jj * D;

@@ -334,12 +334,12 @@ def test_zero_filled_tail_without_mask_would_leak(oracle_lib):
 # --------------------------------------------------------------------------
 
 MUTANTS = {
-    "diagonal_excluded": ("return (i + 1 < Lk) ? i + 1 : Lk;",
-                          "return (i < Lk) ? i : Lk;"),
-    "causal_ignored": ("if (!causal) return Lk;", "return Lk;"),
+    "diagonal_excluded": ("if (causal && i + 1 < e) e = i + 1;",
+                          "if (causal && i < e) e = i;"),
+    "causal_ignored": ("if (causal && i + 1 < e) e = i + 1;", ""),
     "max_not_subtracted": ("p[j] = exp(p[j] - m);", "p[j] = exp(p[j]);"),
     "exp_sign_flipped": ("p[j] = exp(p[j] - m);", "p[j] = exp(m - p[j]);"),
-    "not_normalised": ("for (j = 0; j < jend; ++j) p[j] /= l;", ""),
+    "not_normalised": ("for (j = jbeg; j < jend; ++j) p[j] /= l;", ""),
     "k_transposed": ("for (d = 0; d < D; ++d) dot += q_row[d] * k_row[d];",
                      "for (d = 0; d < D; ++d) dot += q_row[d] * "
                      "k_head[(d * Lk + j) % (Lk * D)]; (void)k_row;"),
