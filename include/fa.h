@@ -44,7 +44,9 @@ enum fa_status {
     FA_ERR_ALIGN = 6,     /* a tensor not 16-byte aligned, lse/delta not 4-byte */
     FA_ERR_ALIAS = 7,     /* an output overlaps an input or another output */
     FA_ERR_POINTER = 8,   /* a pointer is not device memory of this device */
-    FA_ERR_LAUNCH = 9     /* the HIP runtime rejected the kernel launch */
+    FA_ERR_LAUNCH = 9,    /* the HIP runtime rejected the kernel launch */
+    FA_ERR_STRIDE = 10    /* fa_fwd_ex: a stride is negative or too large, or o
+                             is a view whose elements overlap */
 };
 
 /* Size limits checked by fa_fwd (FA_ERR_SHAPE past them). */
@@ -139,6 +141,42 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            const float *lse, const void *dout, void *dq, void *dk, void *dv,
            float *delta, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
            int64_t D, int causal, float scale, int dtype, void *stream);
+
+/*
+ * fa_fwd_ex -- the forward of fa_fwd on strided views and with an optional
+ * local (sliding-window) mask, enqueued on `stream`.
+ *
+ * The FlashAttention-2 forward article's host wrapper hands the kernel the
+ * batch, head, sequence and feature strides of Q, K, V and O, and the kernel
+ * addresses every block with them (the wrapper and the kernel's offset
+ * arithmetic).  Here the feature dimension must be contiguous (stride 1,
+ * which the 16-byte vector loads need); the other three strides are free.
+ * The article leaves other mask variants for later; the local window is the
+ * common one: query i keeps key j only when i - window_left <= j and
+ * j <= i + window_right.
+ *
+ * strides  12 int64 values, in elements: q (batch, head, row), then k, v,
+ *          o in the same order.  Element (b, h, i, d) of q is at
+ *          q + b*strides[0] + h*strides[1] + i*strides[2] + d.  For the
+ *          [B, L, H, D] layout (sequence before heads) pass
+ *          (L*H*D, D, H*D).  Every stride must be >= 0, at most 2^40, row
+ *          strides at most 2^24, and a multiple of 8 elements (bf16/fp16) or
+ *          4 (fp32) so rows stay 16-byte aligned; o must not map two elements
+ *          to one address.  Inputs may overlap each other (packed QKV).
+ * causal, window_left, window_right
+ *          the keep rule is the conjunction of: (causal == 0 or j <= i),
+ *          (window_left < 0 or j >= i - window_left),
+ *          (window_right < 0 or j <= i + window_right).  A row that keeps no
+ *          key gets o = 0 and lse = -inf.
+ * lse      contiguous [B, H, Lq] fp32 as for fa_fwd, or NULL.
+ * Other arguments, semantics, precision, ownership and errors as fa_fwd;
+ * FA_ERR_STRIDE for invalid strides.  A call with the contiguous strides
+ * and no window runs exactly fa_fwd.
+ */
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+              int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+              const int64_t *strides, int causal, int64_t window_left,
+              int64_t window_right, float scale, int dtype, void *stream);
 
 /* Static text for a status code ("unknown status" for anything else). */
 const char *fa_status_string(int status);

@@ -10,10 +10,10 @@ from __future__ import annotations
 import math
 
 from ._lib import (FA_BF16, FA_F16, FA_F32, FaError, fa_bwd,
-                   fa_bwd_kernel_name, fa_fwd, fa_kernel_name,
+                   fa_bwd_kernel_name, fa_fwd, fa_fwd_ex, fa_kernel_name,
                    fa_status_string, fa_version, load)
 
-__all__ = ["forward", "backward", "fa_fwd", "fa_bwd", "fa_kernel_name",
+__all__ = ["forward", "backward", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_kernel_name",
            "fa_bwd_kernel_name", "fa_status_string", "fa_version", "FaError",
            "dtype_code", "load"]
 
@@ -29,13 +29,19 @@ def dtype_code(dtype) -> int:
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None,
-            out=None, lse=None, want_lse: bool = True, stream=None):
+            out=None, lse=None, want_lse: bool = True, stream=None,
+            window=None):
     """Attention forward on the current (or given) stream.
 
-    q [B,H,Lq,D], k/v [B,H,Lk,D] CUDA (HIP) tensors of one dtype, contiguous.
-    ``scale`` defaults to 1/sqrt(D).  Returns (o, lse) with o like q and lse
-    fp32 [B,H,Lq] (None when ``want_lse`` is False).  ``out``/``lse`` may be
-    preallocated.  Raises FaError on a status other than FA_OK.
+    q [B,H,Lq,D], k/v [B,H,Lk,D] CUDA (HIP) tensors of one dtype.  Views
+    with any (batch, head, row) strides work as long as D is contiguous (for
+    example a [B,L,H,D] tensor transposed to [B,H,L,D]); they, and a local
+    ``window=(left, right)`` (query i keeps keys i-left .. i+right; None or
+    a negative bound: no bound), go through ``fa_fwd_ex``, everything else
+    through ``fa_fwd``.  ``scale`` defaults to 1/sqrt(D).  Returns (o, lse)
+    with o laid out like q (``empty_like``) and lse fp32 [B,H,Lq] (None when
+    ``want_lse`` is False).  ``out``/``lse`` may be preallocated.  Raises
+    FaError on a status other than FA_OK.
     """
     import torch
     load()
@@ -44,8 +50,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None,
             raise ValueError(f"{name} must be a device tensor")
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, L, D]")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
     B, H, Lq, D = q.shape
@@ -60,10 +66,22 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None,
         lse = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                lse.data_ptr() if lse is not None else None, B, H, Lq, Lk, D,
-                int(bool(causal)), float(scale), dtype_code(q.dtype),
-                stream.cuda_stream)
+    if out.stride(3) != 1 or tuple(out.shape) != (B, H, Lq, D):
+        raise ValueError("out must be [B, H, Lq, D] with a contiguous last dimension")
+    wl, wr = (-1, -1) if window is None else (
+        -1 if window[0] is None else int(window[0]),
+        -1 if window[1] is None else int(window[1]))
+    general = (not all(t.is_contiguous() for t in (q, k, v, out))) or wl >= 0 or wr >= 0
+    lse_ptr = lse.data_ptr() if lse is not None else None
+    if general:
+        strides = [x for t in (q, k, v, out) for x in t.stride()[:3]]
+        rc = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                       lse_ptr, B, H, Lq, Lk, D, strides, int(bool(causal)), wl, wr,
+                       float(scale), dtype_code(q.dtype), stream.cuda_stream)
+    else:
+        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                    lse_ptr, B, H, Lq, Lk, D, int(bool(causal)), float(scale),
+                    dtype_code(q.dtype), stream.cuda_stream)
     if rc != 0:
         raise FaError(rc, fa_status_string(rc))
     return out, lse

@@ -1,6 +1,6 @@
 """ctypes binding of libfa.so: argument marshalling only.
 
-The names match the C ABI in include/fa.h (``fa_fwd``, ``fa_bwd``,
+The names match the C ABI in include/fa.h (``fa_fwd``, ``fa_fwd_ex``, ``fa_bwd``,
 ``fa_status_string``, ``fa_kernel_name``, ``fa_bwd_kernel_name``,
 ``fa_version``).  Every step of the attention forward and backward runs in
 the HIP kernels; there is no Python or CPU fallback, and loading
@@ -18,7 +18,7 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM",
     4: "FA_ERR_DTYPE", 5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS",
-    8: "FA_ERR_POINTER", 9: "FA_ERR_LAUNCH",
+    8: "FA_ERR_POINTER", 9: "FA_ERR_LAUNCH", 10: "FA_ERR_STRIDE",
 }
 
 _lib = None
@@ -46,6 +46,10 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                            ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                              ctypes.POINTER(ctypes.c_int64), ctypes.c_int, i64,
+                              i64, ctypes.c_float, ctypes.c_int, vp]
+    lib.fa_fwd_ex.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [vp] * 10 + [i64] * 5 + [
         ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.fa_bwd.restype = ctypes.c_int
@@ -69,6 +73,18 @@ def fa_fwd(q: int, k: int, v: int, o: int, lse: int | None, B: int, H: int,
     """Raw call: integer device addresses in, status code out."""
     return load().fa_fwd(q, k, v, o, lse, B, H, Lq, Lk, D, int(causal),
                          float(scale), int(dtype), stream)
+
+
+def fa_fwd_ex(q: int, k: int, v: int, o: int, lse: int | None, B: int, H: int,
+              Lq: int, Lk: int, D: int, strides, causal: int,
+              window_left: int, window_right: int, scale: float, dtype: int,
+              stream: int | None) -> int:
+    """Raw call: device addresses, 12 element strides (q, k, v, o; each
+    batch, head, row), window bounds (-1: none); status code out."""
+    arr = (ctypes.c_int64 * 12)(*[int(x) for x in strides]) if strides is not None else None
+    return load().fa_fwd_ex(q, k, v, o, lse, B, H, Lq, Lk, D, arr, int(causal),
+                            int(window_left), int(window_right), float(scale),
+                            int(dtype), stream)
 
 
 def fa_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int,

@@ -53,6 +53,8 @@ bool is_device_ptr(const void *p, int device)
     return attr.type == hipMemoryTypeDevice && attr.device == device;
 }
 
+int launch_forward(const fa::FwdArgs &a);
+
 fa::FwdArgs make_args(const void *q, const void *k, const void *v, void *o, float *lse,
                       int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, int causal,
                       float scale, int dtype, void *stream)
@@ -72,7 +74,56 @@ fa::FwdArgs make_args(const void *q, const void *k, const void *v, void *o, floa
     a.scale = scale;
     a.dtype = dtype;
     a.stream = static_cast<hipStream_t>(stream);
+    // contiguous [B, H, L, D]
+    const int64_t qs[3] = {H * Lq * D, Lq * D, D}, ks[3] = {H * Lk * D, Lk * D, D};
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = qs[i];
+        a.os[i] = qs[i];
+        a.ks[i] = ks[i];
+        a.vs[i] = ks[i];
+    }
+    a.wl = -1;
+    a.wr = -1;
+    a.general = false;
     return a;
+}
+
+// Byte length of a strided [B, H, L, D] view (D contiguous) from its base.
+int64_t view_bytes(int64_t B, int64_t H, int64_t L, int64_t D, const int64_t *s, int64_t es)
+{
+    return ((B - 1) * s[0] + (H - 1) * s[1] + (L - 1) * s[2] + D) * es;
+}
+
+// No two elements of the view share an address: with the dimensions in
+// increasing stride order (D first, stride 1), every stride of a dimension
+// longer than one is at least the span of the smaller dimensions.
+bool view_injective(int64_t B, int64_t H, int64_t L, int64_t D, const int64_t *s)
+{
+    int64_t st[3] = {s[0], s[1], s[2]}, sz[3] = {B, H, L};
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (st[j] < st[i]) {
+                int64_t t = st[i];
+                st[i] = st[j];
+                st[j] = t;
+                t = sz[i];
+                sz[i] = sz[j];
+                sz[j] = t;
+            }
+    int64_t span = D;
+    for (int i = 0; i < 3; ++i) {
+        if (sz[i] == 1) continue;
+        if (st[i] < span) return false;
+        span = st[i] * (sz[i] - 1) + span;
+    }
+    return true;
+}
+
+// The contiguous strides of a [B, H, L, D] tensor (dimensions of length one
+// may carry any stride).
+bool is_contiguous(int64_t B, int64_t H, int64_t L, int64_t D, const int64_t *s)
+{
+    return (B == 1 || s[0] == H * L * D) && (H == 1 || s[1] == L * D) && (L == 1 || s[2] == D);
 }
 
 // Tuning override "NWxQBxBNxOCCxPIPE" (for sweeps), or "valu" to force the
@@ -94,6 +145,22 @@ bool env_tile(fa::MfmaTile &t, bool &force_valu)
     if (n != 9 || x1 != 'x' || x2 != 'x' || x3 != 'x' || x4 != 'x') return false;
     t = fa::MfmaTile{nw, qb, bn, occ, pipe};
     return true;
+}
+
+// Kernel choice for a validated forward call.
+int launch_forward(const fa::FwdArgs &a)
+{
+    fa::MfmaTile tile{};
+    bool force_valu = false;
+    const bool have_tile = env_tile(tile, force_valu);
+    hipError_t e;
+    if (force_valu || !fa::mfma_supported(a))
+        e = fa::valu_launch(a);
+    else if (a.general)
+        e = fa::mfma_launch_general(a);
+    else
+        e = fa::mfma_launch(a, have_tile ? tile : fa::mfma_choose_tile(a));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -130,15 +197,61 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
 
     const fa::FwdArgs a = make_args(q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, dtype,
                                     stream);
-    fa::MfmaTile tile{};
-    bool force_valu = false;
-    const bool have_tile = env_tile(tile, force_valu);
-    hipError_t e;
-    if (!force_valu && fa::mfma_supported(a))
-        e = fa::mfma_launch(a, have_tile ? tile : fa::mfma_choose_tile(a));
-    else
-        e = fa::valu_launch(a);
-    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    return launch_forward(a);
+}
+
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+              int64_t H, int64_t Lq, int64_t Lk, int64_t D, const int64_t *strides, int causal,
+              int64_t window_left, int64_t window_right, float scale, int dtype, void *stream)
+{
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || strides == nullptr)
+        return FA_ERR_NULL;
+    int rc = check_args(B, H, Lq, Lk, D, scale, dtype);
+    if (rc != FA_OK) return rc;
+    const int64_t es = dtype == FA_F32 ? 4 : 2;
+    for (int i = 0; i < 12; ++i) {
+        if (strides[i] < 0 || strides[i] > ((int64_t)1 << 40)) return FA_ERR_STRIDE;
+        if (i % 3 == 2 && strides[i] > ((int64_t)1 << 24)) return FA_ERR_STRIDE;
+    }
+    const int64_t *qs = strides, *ks = strides + 3, *vs = strides + 6, *os = strides + 9;
+    if (!view_injective(B, H, Lq, D, os)) return FA_ERR_STRIDE;
+    for (int i = 0; i < 12; ++i)
+        if ((strides[i] * es) % 16 != 0) return FA_ERR_ALIGN;
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o);
+    if ((mis & 15u) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_ALIGN;
+
+    const int64_t nq = view_bytes(B, H, Lq, D, qs, es), nk = view_bytes(B, H, Lk, D, ks, es),
+                  nv = view_bytes(B, H, Lk, D, vs, es), no = view_bytes(B, H, Lq, D, os, es),
+                  nl = B * H * Lq * 4;
+    if (overlaps(o, no, q, nq) || overlaps(o, no, k, nk) || overlaps(o, no, v, nv) ||
+        overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nv) ||
+        overlaps(lse, nl, o, no))
+        return FA_ERR_ALIAS;
+
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) {
+        (void)hipGetLastError();
+        return FA_ERR_POINTER;
+    }
+    if (!is_device_ptr(q, device) || !is_device_ptr(k, device) || !is_device_ptr(v, device) ||
+        !is_device_ptr(o, device) || (lse != nullptr && !is_device_ptr(lse, device)))
+        return FA_ERR_POINTER;
+
+    fa::FwdArgs a = make_args(q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, dtype, stream);
+    // a window that cannot exclude any key is no window
+    a.wl = (window_left < 0 || window_left >= Lq + Lk) ? -1 : (int)window_left;
+    a.wr = (window_right < 0 || window_right >= Lq + Lk) ? -1 : (int)window_right;
+    const bool contiguous = is_contiguous(B, H, Lq, D, qs) && is_contiguous(B, H, Lk, D, ks) &&
+                            is_contiguous(B, H, Lk, D, vs) && is_contiguous(B, H, Lq, D, os);
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = qs[i];
+        a.ks[i] = ks[i];
+        a.vs[i] = vs[i];
+        a.os[i] = os[i];
+    }
+    a.general = !contiguous || a.wl >= 0 || a.wr >= 0;
+    return launch_forward(a);
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -227,6 +340,7 @@ const char *fa_status_string(int status)
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_POINTER: return "a pointer is not device memory of the current device";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_STRIDE: return "a stride is negative or too large, or o has overlapping elements";
     default: return "unknown status";
     }
 }

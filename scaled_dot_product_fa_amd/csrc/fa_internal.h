@@ -7,7 +7,11 @@
 
 namespace fa {
 
-// Arguments of one forward call after validation.
+// Arguments of one forward call after validation.  Strides are in elements
+// (batch, head, row) per tensor, the head dimension is contiguous; fa_fwd
+// fills in the contiguous [B, H, L, D] strides.  wl / wr: local window
+// bounds (query i keeps key j when i - wl <= j <= i + wr), -1 = no bound.
+// general: strides are not the contiguous ones or a window is set.
 struct FwdArgs {
     const void *q, *k, *v;
     void *o;
@@ -17,6 +21,9 @@ struct FwdArgs {
     float scale;
     int dtype;
     hipStream_t stream;
+    int64_t qs[3], ks[3], vs[3], os[3];
+    int wl, wr;
+    bool general;
 };
 
 // Tile shape of the MFMA kernel: NW waves per workgroup, each wave owning
@@ -36,6 +43,10 @@ bool mfma_supported(const FwdArgs &a);
 MfmaTile mfma_choose_tile(const FwdArgs &a);
 const char *mfma_kernel_name(const FwdArgs &a, const MfmaTile &t);
 hipError_t mfma_launch(const FwdArgs &a, const MfmaTile &t);
+// Strided / windowed calls: the software-pipelined kernel with runtime
+// strides and window (8 waves when the grid is large, else 4).
+const char *mfma_general_kernel_name(const FwdArgs &a);
+hipError_t mfma_launch_general(const FwdArgs &a);
 
 // Vector-ALU kernel: any I/O type, D in {64, 128}, any finite scale.
 const char *valu_kernel_name(const FwdArgs &a);

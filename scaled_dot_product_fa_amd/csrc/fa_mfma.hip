@@ -126,6 +126,11 @@ struct Params {
     float *lse;
     int BH, Lq, Lk, ntq;
     float scale, c;  // c = scale * log2(e)
+    // strided / windowed calls only (the GEN kernels): heads per batch,
+    // element strides (batch, head, row) of q, k, v, o, window bounds (-1:
+    // none)
+    int H, wl, wr;
+    int64_t qs[3], ks[3], vs[3], os[3];
 };
 
 // Workgroup id -> (head bh, query block qt).  Hardware places workgroup w
@@ -521,7 +526,10 @@ __device__ __forceinline__ void wait_vmcnt()
     __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN, int OCC>
+// GEN: strided views and the local window (runtime strides in Params, key
+// range clipped to the window, window edges masked); otherwise contiguous
+// [B, H, L, D] with compile-time row strides.
+template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN, int OCC, bool GEN = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_fwd_mfma_dma_kernel(Params p)
 {
@@ -559,9 +567,29 @@ void fa_fwd_mfma_dma_kernel(Params p)
     const int q_first = qt * BM;
     const int qw = q_first + wave * QB * 32;   // first query row of this wave
 
-    const uint16_t *qh = p.q + (int64_t)bh * p.Lq * D;
-    const uint16_t *kh = p.k + (int64_t)bh * p.Lk * D;
-    const uint16_t *vh = p.v + (int64_t)bh * p.Lk * D;
+    // per-(b, h) bases and row strides, in elements
+    int64_t q_base, k_base, v_base, o_base;
+    int q_sl, k_sl, v_sl, o_sl;
+    if constexpr (GEN) {
+        const int b = bh / p.H, h = bh % p.H;
+        q_base = b * p.qs[0] + h * p.qs[1];
+        k_base = b * p.ks[0] + h * p.ks[1];
+        v_base = b * p.vs[0] + h * p.vs[1];
+        o_base = b * p.os[0] + h * p.os[1];
+        q_sl = (int)p.qs[2];
+        k_sl = (int)p.ks[2];
+        v_sl = (int)p.vs[2];
+        o_sl = (int)p.os[2];
+    } else {
+        q_base = (int64_t)bh * p.Lq * D;
+        k_base = (int64_t)bh * p.Lk * D;
+        v_base = k_base;
+        o_base = q_base;
+        q_sl = k_sl = v_sl = o_sl = D;
+    }
+    const uint16_t *qh = p.q + q_base;
+    const uint16_t *kh = p.k + k_base;
+    const uint16_t *vh = p.v + v_base;
 
     // ---- Q^T operand in VGPRs (rows past Lq read the last row; not stored)
     u32x4 qreg[QB][DC];
@@ -570,7 +598,7 @@ void fa_fwd_mfma_dma_kernel(Params p)
         const int row = min(qw + b * 32 + l32, p.Lq - 1);
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
-            qreg[b][dc] = *reinterpret_cast<const u32x4 *>(qh + (uint32_t)row * D + dc * 16 + hi * 8);
+            qreg[b][dc] = *reinterpret_cast<const u32x4 *>(qh + (int64_t)row * q_sl + dc * 16 + hi * 8);
     }
 
     // ---- per-lane DMA source offsets (bytes within a tile) and LDS slots
@@ -581,11 +609,11 @@ void fa_fwd_mfma_dma_kernel(Params p)
         const int slot = (r * NW + wave) * 64 + lane;
         const int row = slot / KCH, pc = slot % KCH;
         ld_row[r] = row;
-        ld_k[r] = (uint32_t)(row * D + (pc ^ swz_k<D>(row)) * 8) * 2;
-        ld_v[r] = (uint32_t)(row * D + (pc ^ swz_v<D>(row)) * 8) * 2;
+        ld_k[r] = (uint32_t)(row * k_sl + (pc ^ swz_k<D>(row)) * 8) * 2;
+        ld_v[r] = (uint32_t)(row * v_sl + (pc ^ swz_v<D>(row)) * 8) * 2;
     }
-    auto issue_one = [&](const uint16_t *src, const uint32_t *offs, int k0, uint8_t *dst) {
-        const uint8_t *t = reinterpret_cast<const uint8_t *>(src + (int64_t)k0 * D);
+    auto issue_one = [&](const uint16_t *src, const uint32_t *offs, int sl, int k0, uint8_t *dst) {
+        const uint8_t *t = reinterpret_cast<const uint8_t *>(src + (int64_t)k0 * sl);
         // wave-uniform LDS base of this wave's 1 KB slots (an SGPR)
         const uint32_t dbase = (uint32_t)__builtin_amdgcn_readfirstlane(
             (int)(lds_addr(dst) + (uint32_t)(wave * 1024)));
@@ -602,13 +630,13 @@ void fa_fwd_mfma_dma_kernel(Params p)
             if (ld_row[r] > last) {
                 // past the end of the keys: fetch any valid row (its scores
                 // are masked and its V rows get probability 0)
-                o -= (uint32_t)(ld_row[r] - last) * ROWB;
+                o -= (uint32_t)(ld_row[r] - last) * (uint32_t)(sl * 2);
             }
             dma_16B(t + o, dbase + (uint32_t)(r * NW * 1024));
         }
     };
-    auto issue_k = [&](int k0, uint8_t *kd) { issue_one(kh, ld_k, k0, kd); };
-    auto issue_v = [&](int k0, uint8_t *vd) { issue_one(vh, ld_v, k0, vd); };
+    auto issue_k = [&](int k0, uint8_t *kd) { issue_one(kh, ld_k, k_sl, k0, kd); };
+    auto issue_v = [&](int k0, uint8_t *vd) { issue_one(vh, ld_v, v_sl, k0, vd); };
 
     // ---- per-lane LDS read offsets (loop invariant)
     uint32_t k_rd[DC];
@@ -645,8 +673,17 @@ void fa_fwd_mfma_dma_kernel(Params p)
     }
     const float c = p.c;
 
-    const int kv_end = CAUSAL ? min(p.Lk, q_first + BM) : p.Lk;
-    const int ntiles = (kv_end + BN - 1) / BN;
+    // keys [kv_begin, kv_end) are visible to some row of the block
+    int kv_begin = 0;
+    int kv_end = CAUSAL ? min(p.Lk, q_first + BM) : p.Lk;
+    if constexpr (GEN) {
+        if (p.wl >= 0) kv_begin = max(0, q_first - p.wl) / BN * BN;
+        if (p.wr >= 0) kv_end = min(kv_end, q_first + BM + p.wr);
+    }
+    const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + BN - 1) / BN : 0;
+    // a block that sees no key still runs the (unused) prologue loads: keep
+    // them on tile 0, so that every issued tile starts below Lk
+    if (ntiles == 0) kv_begin = 0;
 
     struct STile {
         f32x16 v[KB][QB];
@@ -683,9 +720,9 @@ void fa_fwd_mfma_dma_kernel(Params p)
     // LDS-read / VALU interleave of the two straight-line blocks.  Tiles past
     // a wave's diagonal are not skipped: they are fully masked and contribute
     // p = 0.
-    issue_k(0, k_lds0);
-    issue_v(0, v_lds0);
-    if (ntiles > 1) issue_k(BN, k_lds1);
+    issue_k(kv_begin, k_lds0);
+    issue_v(kv_begin, v_lds0);
+    if (ntiles > 1) issue_k(kv_begin + BN, k_lds1);
     sync_tiles();
     STile cur;
     qk_part(cur, k_lds0, 0, NQK);
@@ -700,10 +737,14 @@ void fa_fwd_mfma_dma_kernel(Params p)
 
     auto step = [&](int j, const uint8_t *k_next, const uint8_t *v_cur, uint8_t *k_dma,
                     uint8_t *v_dma) {
-        if (j + 2 < ntiles) issue_k((j + 2) * BN, k_dma);
-        if (j + 1 < ntiles) issue_v((j + 1) * BN, v_dma);
-        const int k0 = j * BN;
-        if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
+        if (j + 2 < ntiles) issue_k(kv_begin + (j + 2) * BN, k_dma);
+        if (j + 1 < ntiles) issue_v(kv_begin + (j + 1) * BN, v_dma);
+        const int k0 = kv_begin + j * BN;
+        bool need_mask = (k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw);
+        if constexpr (GEN)
+            need_mask = need_mask || (p.wr >= 0 && k0 + BN - 1 > qw + p.wr) ||
+                        (p.wl >= 0 && k0 < qw + QB * 32 - 1 - p.wl);
+        if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -711,7 +752,11 @@ void fa_fwd_mfma_dma_kernel(Params p)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int key = k0 + kb * 32 + (i >> 3) * 16 + hi * 8 + (i & 7);
-                        const bool keep = key < p.Lk && (!CAUSAL || key <= qw + b * 32 + l32);
+                        const int qrow = qw + b * 32 + l32;
+                        bool keep = key < p.Lk && (!CAUSAL || key <= qrow);
+                        if constexpr (GEN)
+                            keep = keep && (p.wr < 0 || key <= qrow + p.wr) &&
+                                   (p.wl < 0 || key >= qrow - p.wl);
                         cur.v[kb][b][i] = keep ? cur.v[kb][b][i] : -INFINITY;
                     }
         }
@@ -840,7 +885,7 @@ void fa_fwd_mfma_dma_kernel(Params p)
         const int row = qw + b * 32 + l32;
         if (row < p.Lq) {
             const float inv = l > 0.f ? 1.f / l : 0.f;
-            uint16_t *orow = p.o + ((int64_t)bh * p.Lq + row) * D;
+            uint16_t *orow = p.o + o_base + (int64_t)row * o_sl;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -1257,6 +1302,51 @@ hipError_t launch_dma(const FwdArgs &a)
     return hipGetLastError();
 }
 
+template <typename Ops, int D, bool CAUSAL, int NW>
+hipError_t launch_general_t(const FwdArgs &a)
+{
+    constexpr int BM = NW * 32;
+    Params p;
+    p.q = static_cast<const uint16_t *>(a.q);
+    p.k = static_cast<const uint16_t *>(a.k);
+    p.v = static_cast<const uint16_t *>(a.v);
+    p.o = static_cast<uint16_t *>(a.o);
+    p.lse = a.lse;
+    p.BH = (int)(a.B * a.H);
+    p.Lq = (int)a.Lq;
+    p.Lk = (int)a.Lk;
+    p.ntq = (int)((a.Lq + BM - 1) / BM);
+    p.scale = a.scale;
+    p.c = a.scale * kLog2e;
+    p.H = (int)a.H;
+    p.wl = a.wl;
+    p.wr = a.wr;
+    for (int i = 0; i < 3; ++i) {
+        p.qs[i] = a.qs[i];
+        p.ks[i] = a.ks[i];
+        p.vs[i] = a.vs[i];
+        p.os[i] = a.os[i];
+    }
+    const int64_t nwg = (int64_t)p.BH * p.ntq;
+    hipLaunchKernelGGL((fa_fwd_mfma_dma_kernel<Ops, D, CAUSAL, NW, 1, 64, 2, true>),
+                       dim3((unsigned)nwg), dim3(NW * 64), 0, a.stream, p);
+    return hipGetLastError();
+}
+
+// 8 waves (256 rows per workgroup) once that still gives 512 workgroups,
+// else 4 waves.
+template <typename Ops>
+hipError_t launch_general_ops(const FwdArgs &a)
+{
+    const bool big = a.B * a.H * ((a.Lq + 255) / 256) >= 512;
+    if (a.D == 64) {
+        if (a.causal) return big ? launch_general_t<Ops, 64, true, 8>(a) : launch_general_t<Ops, 64, true, 4>(a);
+        return big ? launch_general_t<Ops, 64, false, 8>(a) : launch_general_t<Ops, 64, false, 4>(a);
+    }
+    if (a.causal) return big ? launch_general_t<Ops, 128, true, 8>(a) : launch_general_t<Ops, 128, true, 4>(a);
+    return big ? launch_general_t<Ops, 128, false, 8>(a) : launch_general_t<Ops, 128, false, 4>(a);
+}
+
 template <typename Ops, int D, bool CAUSAL, int NW, int QB, int BN, int OCC>
 hipError_t launch_cfg(const FwdArgs &a)
 {
@@ -1382,6 +1472,22 @@ const char *mfma_kernel_name(const FwdArgs &a, const MfmaTile &t)
 hipError_t mfma_launch(const FwdArgs &a, const MfmaTile &t)
 {
     return a.dtype == 2 ? launch_ops<Bf16Ops>(a, t) : launch_ops<F16Ops>(a, t);
+}
+
+const char *mfma_general_kernel_name(const FwdArgs &a)
+{
+    static const char *names[2][2][2] = {
+        {{"fa_fwd_mfma_f16_d64_strided", "fa_fwd_mfma_f16_d64_causal_strided"},
+         {"fa_fwd_mfma_f16_d128_strided", "fa_fwd_mfma_f16_d128_causal_strided"}},
+        {{"fa_fwd_mfma_bf16_d64_strided", "fa_fwd_mfma_bf16_d64_causal_strided"},
+         {"fa_fwd_mfma_bf16_d128_strided", "fa_fwd_mfma_bf16_d128_causal_strided"}},
+    };
+    return names[a.dtype == 2][a.D == 128][a.causal ? 1 : 0];
+}
+
+hipError_t mfma_launch_general(const FwdArgs &a)
+{
+    return a.dtype == 2 ? launch_general_ops<Bf16Ops>(a) : launch_general_ops<F16Ops>(a);
 }
 
 }  // namespace fa

@@ -11,7 +11,9 @@
 //
 // Layout: 256 threads = 64 query rows x 4 threads; thread t4 of a row owns
 // head-dimension slice [t4*D/4, (t4+1)*D/4).  Scores are reduced across the
-// 4 threads of a row with lane shuffles.
+// 4 threads of a row with lane shuffles.  Tensors are addressed through
+// (batch, head, row) element strides, so strided views work as they are;
+// an optional local window (keys i - wl .. i + wr) narrows the key range.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -32,12 +34,21 @@ __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
 template <typename T>
 __device__ __forceinline__ T from_f32(float x) { return static_cast<T>(x); }
 
+struct ValuParams {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int H, Lq, Lk, ntq, wl, wr;
+    float scale;
+    int64_t qs[3], ks[3], vs[3], os[3];
+};
+
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kValuThreads) void fa_fwd_valu_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    T *__restrict__ o, float *__restrict__ lse, int Lq, int Lk, float scale,
-    int ntq)
+__global__ __launch_bounds__(kValuThreads) void fa_fwd_valu_kernel(ValuParams p)
 {
+    const int Lq = p.Lq, Lk = p.Lk, ntq = p.ntq;
+    const float scale = p.scale;
+    float *__restrict__ lse = p.lse;
     constexpr int DS = D / 4;  // dims owned by one thread
     __shared__ float ks[kValuBN][D];
     __shared__ float vs[kValuBN][D];
@@ -51,26 +62,32 @@ __global__ __launch_bounds__(kValuThreads) void fa_fwd_valu_kernel(
     const int qi = q_first + row_local;
     const bool row_valid = qi < Lq;
 
-    const T *qh = q + bh * (int64_t)Lq * D;
-    const T *kh = k + bh * (int64_t)Lk * D;
-    const T *vh = v + bh * (int64_t)Lk * D;
+    const int64_t b_ = bh / p.H, h_ = bh % p.H;
+    const T *qh = static_cast<const T *>(p.q) + b_ * p.qs[0] + h_ * p.qs[1];
+    const T *kh = static_cast<const T *>(p.k) + b_ * p.ks[0] + h_ * p.ks[1];
+    const T *vh = static_cast<const T *>(p.v) + b_ * p.vs[0] + h_ * p.vs[1];
+    T *oh = static_cast<T *>(p.o) + b_ * p.os[0] + h_ * p.os[1];
+    const int64_t q_sl = p.qs[2], k_sl = p.ks[2], v_sl = p.vs[2], o_sl = p.os[2];
 
     float qr[DS], acc[DS];
 #pragma unroll
     for (int e = 0; e < DS; ++e) {
-        qr[e] = row_valid ? to_f32(qh[(int64_t)qi * D + t4 * DS + e]) : 0.f;
+        qr[e] = row_valid ? to_f32(qh[(int64_t)qi * q_sl + t4 * DS + e]) : 0.f;
         acc[e] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
 
-    const int kv_end = CAUSAL ? min(Lk, q_first + kValuBM) : Lk;
-    for (int k0 = 0; k0 < kv_end; k0 += kValuBN) {
+    int kv_end = CAUSAL ? min(Lk, q_first + kValuBM) : Lk;
+    int kv_begin = 0;
+    if (p.wl >= 0) kv_begin = max(0, q_first - p.wl) / kValuBN * kValuBN;
+    if (p.wr >= 0) kv_end = min(kv_end, q_first + kValuBM + p.wr);
+    for (int k0 = kv_begin; k0 < kv_end; k0 += kValuBN) {
         __syncthreads();
         for (int idx = tid; idx < kValuBN * D; idx += kValuThreads) {
             const int r = idx / D, c = idx % D;
             const int kr = k0 + r;
-            ks[r][c] = kr < Lk ? to_f32(kh[(int64_t)kr * D + c]) : 0.f;
-            vs[r][c] = kr < Lk ? to_f32(vh[(int64_t)kr * D + c]) : 0.f;
+            ks[r][c] = kr < Lk ? to_f32(kh[(int64_t)kr * k_sl + c]) : 0.f;
+            vs[r][c] = kr < Lk ? to_f32(vh[(int64_t)kr * v_sl + c]) : 0.f;
         }
         __syncthreads();
 
@@ -84,7 +101,8 @@ __global__ __launch_bounds__(kValuThreads) void fa_fwd_valu_kernel(
             part += __shfl_xor(part, 1);
             part += __shfl_xor(part, 2);
             const int kj = k0 + j;
-            const bool keep = kj < Lk && (!CAUSAL || kj <= qi);
+            const bool keep = kj < Lk && (!CAUSAL || kj <= qi) &&
+                              (p.wl < 0 || kj >= qi - p.wl) && (p.wr < 0 || kj <= qi + p.wr);
             s[j] = keep ? part * scale : -INFINITY;
             tmax = fmaxf(tmax, s[j]);
         }
@@ -109,7 +127,7 @@ __global__ __launch_bounds__(kValuThreads) void fa_fwd_valu_kernel(
 
     if (row_valid) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        T *orow = o + (bh * (int64_t)Lq + qi) * D + t4 * DS;
+        T *orow = oh + (int64_t)qi * o_sl + t4 * DS;
 #pragma unroll
         for (int e = 0; e < DS; ++e) orow[e] = from_f32<T>(acc[e] * inv);
         if (lse != nullptr && t4 == 0)
@@ -120,13 +138,28 @@ __global__ __launch_bounds__(kValuThreads) void fa_fwd_valu_kernel(
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_t(const FwdArgs &a)
 {
-    const int ntq = (int)((a.Lq + kValuBM - 1) / kValuBM);
-    const int64_t nwg = a.B * a.H * ntq;
+    ValuParams p;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.o = a.o;
+    p.lse = a.lse;
+    p.H = (int)a.H;
+    p.Lq = (int)a.Lq;
+    p.Lk = (int)a.Lk;
+    p.ntq = (int)((a.Lq + kValuBM - 1) / kValuBM);
+    p.wl = a.wl;
+    p.wr = a.wr;
+    p.scale = a.scale;
+    for (int i = 0; i < 3; ++i) {
+        p.qs[i] = a.qs[i];
+        p.ks[i] = a.ks[i];
+        p.vs[i] = a.vs[i];
+        p.os[i] = a.os[i];
+    }
+    const int64_t nwg = a.B * a.H * p.ntq;
     hipLaunchKernelGGL((fa_fwd_valu_kernel<T, D, CAUSAL>), dim3((unsigned)nwg),
-                       dim3(kValuThreads), 0, a.stream,
-                       static_cast<const T *>(a.q), static_cast<const T *>(a.k),
-                       static_cast<const T *>(a.v), static_cast<T *>(a.o), a.lse,
-                       (int)a.Lq, (int)a.Lk, a.scale, ntq);
+                       dim3(kValuThreads), 0, a.stream, p);
     return hipGetLastError();
 }
 

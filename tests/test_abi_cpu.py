@@ -24,8 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_kernel_name", "fa_fwd",
-                                    "fa_kernel_name", "fa_status_string",
-                                    "fa_version"]
+                                    "fa_fwd_ex", "fa_kernel_name",
+                                    "fa_status_string", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(0, 10):
+    for code in range(0, 11):
         s = fa.fa_status_string(code)
         assert s and s != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -183,3 +183,66 @@ def test_bwd_kernel_selection():
         "fa_bwd_valu_f32_d64_causal"
     assert fa.fa_bwd_kernel_name(1, 2, 128, 128, 65, 0, 1.0, 2) is None
     assert fa.fa_bwd_kernel_name(1, 2, 128, 0, 64, 0, 1.0, 2) is None
+
+
+# ---- fa_fwd_ex: strides and window, host-side validation ------------------
+
+def contig(B, H, L, D):
+    return [H * L * D, L * D, D]
+
+
+def xcall(strides=None, q=Q, k=K, v=V, o=O, lse=L, wl=-1, wr=-1, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    if strides is None:
+        sq = contig(a["B"], a["H"], a["Lq"], a["D"])
+        sk = contig(a["B"], a["H"], a["Lk"], a["D"])
+        strides = sq + sk + sk + sq
+    return fa.fa_fwd_ex(q, k, v, o, lse, a["B"], a["H"], a["Lq"], a["Lk"],
+                        a["D"], strides, a["causal"], wl, wr, a["scale"],
+                        a["dtype"], None)
+
+
+def test_ex_null_strides():
+    assert fa.fa_fwd_ex(Q, K, V, O, L, 1, 2, 128, 128, 64, None, 0, -1, -1,
+                        0.125, 2, None) == 1
+
+
+def test_ex_bad_strides():
+    base = contig(1, 2, 128, 64) * 4
+    for i in range(12):
+        s = list(base)
+        s[i] = -8
+        assert xcall(s) == 10, i
+    s = list(base)
+    s[2] = 1 << 25                       # row stride past 2^24
+    assert xcall(s) == 10
+    s = list(base)
+    s[9:12] = [0, 0, 64]                 # o: every (b, h) on the same rows
+    assert xcall(s) == 10
+    s = list(base)
+    s[11] = 32                           # o rows overlap (row stride < D)
+    assert xcall(s) == 10
+    s = list(base)
+    s[5] = 68                            # k row stride not a multiple of 8
+    assert xcall(s) == 6
+
+
+def test_ex_layouts_pass_validation_until_device_check():
+    # [B, L, H, D] strides are valid; the fake addresses then fail the
+    # device-pointer check (8), i.e. every earlier check passed
+    B, H, L, D = 2, 4, 128, 64
+    blhd = [L * H * D, D, H * D]
+    assert xcall(blhd * 4, B=B, H=H, Lq=L, Lk=L, D=D) == 8
+    # packed QKV: q, k, v interleaved in one [B, L, 3, H, D] buffer
+    pk = [L * 3 * H * D, D, 3 * H * D]
+    assert xcall(pk * 3 + blhd, q=Q, k=Q + 2 * H * D, v=Q + 4 * H * D,
+                 B=B, H=H, Lq=L, Lk=L, D=D) == 8
+    assert xcall(wl=3, wr=0, causal=1) == 8
+
+
+def test_ex_output_overlapping_input_rejected():
+    nbytes = 1 * 2 * 128 * 64 * 2
+    assert xcall(o=Q + 16) == 7
+    assert xcall(o=K + nbytes - 16) == 7
+    assert xcall(lse=O) == 7
