@@ -60,25 +60,53 @@ def workload_desc(w, causal):
             f"{'causal' if causal else 'non-causal'}")
 
 
-def time_forward(w, causal, steps, warmup):
-    """Returns dict with wall ms/step, event ms/launch, flops and buffers."""
+def visible_pairs(Lq, Lk, causal, window):
+    """Number of (query, key) pairs the mask keeps."""
+    import numpy as np
+    i = np.arange(Lq, dtype=np.int64)
+    lo = np.zeros(Lq, dtype=np.int64)
+    hi = np.full(Lq, Lk - 1, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, i)
+    if window is not None and window[0] >= 0:
+        lo = np.maximum(lo, i - window[0])
+    if window is not None and window[1] >= 0:
+        hi = np.minimum(hi, i + window[1])
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def time_forward(w, causal, steps, warmup, layout="bhld", window=None):
+    """Returns dict with wall ms/step, event ms/launch, flops and buffers.
+    layout "blhd": the inputs live in [B, L, H, D] buffers (viewed as
+    [B, H, L, D]); window (left, right): local mask.  Both go through
+    fa_fwd_ex; FLOPs are then 4*D per kept (query, key) pair."""
     import torch
     import scaled_dot_product_fa_amd as fa
     from scaled_dot_product_fa_amd import inputs
 
     dev = torch.device("cuda:0")
     q, k, v = inputs.workload_inputs(w)
-    dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
+    if layout == "blhd":
+        dq, dk, dv = (t.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+                      for t in (q, k, v))
+    else:
+        dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
     o = torch.empty_like(dq)
     lse = torch.empty((w.B, w.H, w.Lq), device=dev, dtype=torch.float32)
     stream = torch.cuda.current_stream(dev)
     name = fa.fa_kernel_name(w.B, w.H, w.Lq, w.Lk, w.D, int(causal), w.scale,
                              fa.dtype_code(dq.dtype))
+    general = layout != "bhld" or window is not None
+    if general:
+        name = f"{name} via fa_fwd_ex ({layout}, window {window})"
+        flops = 4.0 * w.B * w.H * w.D * visible_pairs(w.Lq, w.Lk, causal, window)
+    else:
+        flops = w.flops(causal)
     log(f"bench: {workload_desc(w, causal)} kernel={name} warmup={warmup} "
         f"steps={steps}")
     for _ in range(warmup):
         fa.forward(dq, dk, dv, causal=causal, scale=w.scale, out=o, lse=lse,
-                   stream=stream)
+                   stream=stream, window=window)
     torch.cuda.synchronize(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -86,14 +114,14 @@ def time_forward(w, causal, steps, warmup):
     ev0.record(stream)
     for _ in range(steps):
         fa.forward(dq, dk, dv, causal=causal, scale=w.scale, out=o, lse=lse,
-                   stream=stream)
+                   stream=stream, window=window)
     ev1.record(stream)
     torch.cuda.synchronize(dev)
     t1 = time.perf_counter()
     return dict(wall_ms=(t1 - t0) * 1e3 / steps,
                 kernel_ms=ev0.elapsed_time(ev1) / steps,
-                flops=w.flops(causal), bytes=w.io_bytes(), kernel=name,
-                q=q, k=k, v=v, o=o, lse=lse)
+                flops=flops, bytes=w.io_bytes(), kernel=name,
+                q=q, k=k, v=v, o=o.contiguous(), lse=lse, window=window)
 
 
 def time_backward(w, causal, steps, warmup):
@@ -193,8 +221,10 @@ def parity_rows(w, causal, r, n_random=8):
     ids = inputs.sample_rows(w.B, w.H, w.Lq, n_random=n_random, seed=w.seed,
                              heads=range(0, w.B * w.H, max(1, w.B * w.H // 8)))
     f64 = lambda t: t.to(torch.float64).numpy()
+    win = r.get("window")
+    win = None if win is None else tuple(win)
     ro, rl = oracle.attention_rows(f64(r["q"]), f64(r["k"]), f64(r["v"]),
-                                   ids.numpy(), causal, w.scale)
+                                   ids.numpy(), causal, w.scale, window=win)
     go = f64(r["o"].cpu().reshape(-1, w.D)[ids])
     gl = r["lse"].cpu().reshape(-1)[ids].double().numpy()
     return dict(rows=int(ids.numel()),
@@ -203,24 +233,33 @@ def parity_rows(w, causal, r, n_random=8):
 
 
 def cpu_baseline(w, causal, r, budget_s=15.0):
-    """The fp64 oracle on a bounded, seeded row sample of the same workload,
-    throughput scaled to TFLOP/s by the same FLOP formula (per row:
-    4*Lk_visible*D)."""
+    """The fp64 oracle on a bounded, seeded row sample of the same workload
+    (same mask), throughput scaled to TFLOP/s by the same FLOP formula (per
+    row: 4*D*visible keys)."""
     import numpy as np
     import torch
     import oracle
     f64 = lambda t: t.to(torch.float64).numpy()
     q, k, v = f64(r["q"]), f64(r["k"]), f64(r["v"])
+    win = r.get("window")
+    win = None if win is None else tuple(win)
     g = np.random.default_rng(w.seed)
     total_rows = w.B * w.H * w.Lq
 
     def run(n):
         ids = np.sort(g.choice(total_rows, size=n, replace=False))
-        vis = (np.minimum(ids % w.Lq + 1, w.Lk) if causal
-               else np.full(n, w.Lk))
-        fl = float((4.0 * vis * w.D).sum())
+        i = ids % w.Lq
+        lo = np.zeros(n, dtype=np.int64)
+        hi = np.full(n, w.Lk - 1, dtype=np.int64)
+        if causal:
+            hi = np.minimum(hi, i)
+        if win is not None and win[0] >= 0:
+            lo = np.maximum(lo, i - win[0])
+        if win is not None and win[1] >= 0:
+            hi = np.minimum(hi, i + win[1])
+        fl = float((4.0 * np.maximum(hi - lo + 1, 0) * w.D).sum())
         t0 = time.perf_counter()
-        oracle.attention_rows(q, k, v, ids, causal, w.scale)
+        oracle.attention_rows(q, k, v, ids, causal, w.scale, window=win)
         return fl, time.perf_counter() - t0
 
     pilot = 2048
@@ -230,7 +269,7 @@ def cpu_baseline(w, causal, r, budget_s=15.0):
     return dict(value=fl / dt / 1e12, unit="TFLOP/s",
                 cores=oracle.num_threads(), kind="oracle",
                 sample=(f"{n} seeded query rows of {workload_desc(w, causal)} "
-                        f"(all keys per row), fp64, {dt:.1f} s"),
+                        f"(all visible keys per row), fp64, {dt:.1f} s"),
                 seconds=dt)
 
 
@@ -259,6 +298,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time fa_bwd (gradients) instead of the forward")
+    ap.add_argument("--layout", choices=("bhld", "blhd"), default="bhld",
+                    help="forward inputs in [B,H,L,D] (default) or in "
+                         "[B,L,H,D] buffers (strided views, fa_fwd_ex)")
+    ap.add_argument("--window", default=None, metavar="LEFT,RIGHT",
+                    help="forward with a local window (fa_fwd_ex); -1 = no "
+                         "bound on that side")
     ap.add_argument("--secondary", action="store_true",
                     help="also time the 16K non-causal forward (the other "
                          "shape the metric names); off by default so that a "
@@ -297,7 +342,11 @@ def main():
     if args.backward:
         main_backward(args, w, causal)
         return
-    r = time_forward(w, causal, args.steps, args.warmup)
+    window = None
+    if args.window is not None:
+        wl, wr = (int(x) for x in args.window.split(","))
+        window = (wl, wr)
+    r = time_forward(w, causal, args.steps, args.warmup, args.layout, window)
     tflops = r["flops"] / (r["wall_ms"] * 1e-3) / 1e12
     k_tflops = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
     log(f"bench: wall {r['wall_ms']:.4f} ms/step, kernel {r['kernel_ms']:.4f} "
@@ -316,7 +365,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else w.dtype,
         "data": "synthetic",
-        "config": {"workload": workload_desc(w, causal), "B": w.B, "H": w.H,
+        "config": {"workload": workload_desc(w, causal)
+                   + ("" if args.layout == "bhld" and window is None
+                      else f" {args.layout} window={window}"), "B": w.B, "H": w.H,
                    "Lq": w.Lq, "Lk": w.Lk, "D": w.D, "causal": causal,
                    "scale": w.scale, "io_dtype": w.dtype,
                    "kernel": r["kernel"]},
