@@ -1399,8 +1399,9 @@ template <typename Ops>
 hipError_t launch_ops(const FwdArgs &a, const MfmaTile &t)
 {
     if (t.pipe == 3) {
-        // 8 waves; 64-key tiles, or 128-key tiles at D = 64 (six buffers of
-        // 32 KB would not fit the LDS at D = 128)
+        // 8 waves; 64-key tiles, 96-key tiles at D = 128 (six buffers of 24
+        // KB), or 128-key tiles at D = 64 (six buffers of 32 KB would not
+        // fit the LDS at D = 128)
         if (!(t.nw == 8 && t.qb == 1 && t.occ == 2)) return hipErrorInvalidConfiguration;
         if (a.D == 64) {
             if (t.bn == 128)
@@ -1409,6 +1410,8 @@ hipError_t launch_ops(const FwdArgs &a, const MfmaTile &t)
                 return a.causal ? launch_pp<Ops, 64, true, 64>(a) : launch_pp<Ops, 64, false, 64>(a);
             return hipErrorInvalidConfiguration;
         }
+        if (t.bn == 96)
+            return a.causal ? launch_pp<Ops, 128, true, 96>(a) : launch_pp<Ops, 128, false, 96>(a);
         if (t.bn != 64) return hipErrorInvalidConfiguration;
         return a.causal ? launch_pp<Ops, 128, true, 64>(a) : launch_pp<Ops, 128, false, 64>(a);
     }
@@ -1435,9 +1438,10 @@ MfmaTile mfma_choose_tile(const FwdArgs &a)
 {
     // Static table from an offline sweep of every tile over shape classes
     // (scaled_dot_product_fa_amd/tune.py, timings in tiles.json).  In short:
-    // the ping-pong kernel (8 waves, 256 query rows; 64-key tiles at
+    // the ping-pong kernel (8 waves, 256 query rows; 96-key tiles at
     // D = 128, 128-key tiles at D = 64) once there are 512+ blocks of 256
-    // rows and 2048+ visible keys per row; otherwise 4 waves of the
+    // rows and 2048+ visible keys per row; at D = 128 non-causal also the
+    // 64-key ping-pong kernel from 128 blocks; otherwise 4 waves of the
     // software-pipelined kernel (128 rows per workgroup, twice as many
     // workgroups).
     struct TileRule {

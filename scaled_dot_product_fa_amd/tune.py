@@ -32,7 +32,7 @@ TABLE_INC = os.path.join(PKG, "csrc", "fa_tiles.inc")
 TILES = {
     64: ["8x1x128x2x3", "8x1x64x2x3", "8x1x64x2x2", "4x1x64x2x2", "4x2x64x1x2",
          "8x1x64x2x0", "4x1x64x2x0", "4x1x64x1x0", "4x2x64x1x0"],
-    128: ["8x1x64x2x3", "8x1x64x2x2", "4x1x64x2x2", "4x2x64x1x2",
+    128: ["8x1x96x2x3", "8x1x64x2x3", "8x1x64x2x2", "4x1x64x2x2", "4x2x64x1x2",
           "8x1x64x2x0", "4x1x64x2x0", "4x1x64x1x0", "4x2x64x1x0"],
 }
 

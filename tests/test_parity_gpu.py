@@ -119,11 +119,13 @@ def test_ragged(shape, causal):
 
 @pytest.mark.parametrize("tile", ["4x1x64x1x0", "4x1x64x2x0", "8x1x64x2x0", "4x2x64x1x0",
                                   "8x1x64x2x2", "4x1x64x2x2", "4x2x64x1x2", "8x1x64x2x3", "8x1x128x2x3",
-                                  "valu"])
+                                  "8x1x96x2x3", "valu"])
 @pytest.mark.parametrize("D,dt", [(64, "bf16"), (128, "f16")])
 def test_tile_variants(tile, D, dt, monkeypatch):
     if tile == "8x1x128x2x3" and D == 128:
         pytest.skip("128-key ping-pong tiles are built for D=64 only (LDS)")
+    if tile == "8x1x96x2x3" and D == 64:
+        pytest.skip("96-key ping-pong tiles are built for D=128 only (1.5 loads per lane at D=64)")
     monkeypatch.setenv("FA_TILE", tile)
     for causal in (False, True):
         q, k, v = inputs.make_qkv(2, 2, 300, 450, D, dt, seed=D + len(tile))
@@ -134,8 +136,10 @@ def test_tile_variants(tile, D, dt, monkeypatch):
 # slot: cover every way the loop can end (1..5 key tiles, ragged and exact)
 # and query blocks shorter than one workgroup.
 @pytest.mark.parametrize("tile,D,dt", [("8x1x64x2x3", 128, "bf16"), ("8x1x64x2x3", 64, "f16"),
-                                       ("8x1x128x2x3", 64, "bf16")])
-@pytest.mark.parametrize("Lk", [1, 63, 64, 65, 128, 129, 192, 193, 256, 257, 320, 449, 769, 833])
+                                       ("8x1x128x2x3", 64, "bf16"), ("8x1x96x2x3", 128, "bf16"),
+                                       ("8x1x96x2x3", 128, "f16")])
+@pytest.mark.parametrize("Lk", [1, 63, 64, 65, 95, 96, 97, 128, 129, 191, 192, 193, 256, 257,
+                                288, 289, 320, 449, 769, 833])
 def test_pingpong_tile_counts(Lk, tile, D, dt, monkeypatch):
     monkeypatch.setenv("FA_TILE", tile)
     for Lq, causal in ((1, False), (257, False), (300, True)):
