@@ -76,6 +76,12 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 #ifndef BWD_KV_VPER
 #define BWD_KV_VPER 10
 #endif
+#ifndef BWD_Q_NW64
+#define BWD_Q_NW64 4
+#endif
+#ifndef BWD_Q_NW128
+#define BWD_Q_NW128 4
+#endif
 #ifndef BWD_Q_OCC64
 #define BWD_Q_OCC64 2
 #endif
@@ -492,13 +498,12 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per 128 query rows, 32 per wave; key tiles of 64.
+// dQ: one workgroup per NW * 32 query rows, 32 per wave; key tiles of 64.
 // ---------------------------------------------------------------------------
-template <typename Ops, int D, bool CAUSAL, int OCC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+template <typename Ops, int D, bool CAUSAL, int OCC, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_bwd_dq_mfma_kernel(BwdParams p)
 {
-    constexpr int NW = kThreads / 64;
     constexpr int BM = NW * 32;          // query rows per workgroup
     constexpr int BN = 64;               // keys per tile
     constexpr int KB = BN / 32, KC = BN / 16;
@@ -506,9 +511,9 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
     constexpr int ROWB = D * 2;
     constexpr int CH = D / 8;
     constexpr int TILEB = BN * ROWB;
-    constexpr int NLD = BN * CH / kThreads;
+    constexpr int NLD = BN * CH / (NW * 64);
     constexpr int BUFB = 2 * TILEB;
-    static_assert(NLD >= 1 && BN * CH % kThreads == 0, "tile split");
+    static_assert(NLD >= 1 && BN * CH % (NW * 64) == 0, "tile split");
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUFB];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -670,9 +675,10 @@ hipError_t launch_t(const BwdArgs &a)
                        dim3((unsigned)(p.BH * p.nt)), dim3(kThreads), 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    p.nt = (int)((a.Lq + BLK - 1) / BLK);
-    hipLaunchKernelGGL((fa_bwd_dq_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_Q_OCC64 : BWD_Q_OCC128>),
-                       dim3((unsigned)(p.BH * p.nt)), dim3(kThreads), 0, a.stream, p);
+    constexpr int NWQ = D == 64 ? BWD_Q_NW64 : BWD_Q_NW128;
+    p.nt = (int)((a.Lq + NWQ * 32 - 1) / (NWQ * 32));
+    hipLaunchKernelGGL((fa_bwd_dq_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_Q_OCC64 : BWD_Q_OCC128, NWQ>),
+                       dim3((unsigned)(p.BH * p.nt)), dim3(NWQ * 64), 0, a.stream, p);
     return hipGetLastError();
 }
 

@@ -23,12 +23,20 @@
 //     of 8 consecutive keys.  The probabilities, rounded to the I/O type,
 //     are then directly the B operand of O^T += V^T P^T (again
 //     32x32x16), with no data movement between lanes.
-//   * V is transposed while it is staged into LDS (V^T, keys fastest), so the
-//     A operand of the PV product is one 16-byte LDS read per lane.
-//   * Both LDS tiles use XOR swizzles so the 16-byte reads of a wave hit
-//     distinct banks.  Tiles are double-buffered: the global loads of tile
-//     j+1 are issued before the math of tile j and written to the other LDS
-//     buffer after it, one barrier per tile.
+//   * Three kernels share this mapping and differ in how K/V reach LDS and
+//     how the work is overlapped:
+//       - fa_fwd_mfma_kernel (pipe 0): K/V staged through VGPRs, V
+//         transposed while it is stored (V^T, keys fastest) so the PV A
+//         operand is one 16-byte read; two buffers, one barrier per tile;
+//       - fa_fwd_mfma_dma_kernel (pipe 2): K/V loaded straight into LDS
+//         (global_load_lds_dwordx4), V^T read with transposing LDS reads,
+//         the QK^T of tile j+1 software-pipelined under the softmax of tile
+//         j; its GEN instantiation serves strided views and the local window;
+//       - fa_fwd_mfma_pp_kernel (pipe 3): the ping-pong kernel, in which the
+//         two waves of each SIMD alternate MFMA and softmax phases (the
+//         default for large grids; see its own comment).
+//     The LDS tiles use XOR swizzles so the reads of a wave hit distinct
+//     banks.
 //   * exp2 is used with c = scale*log2(e) folded into one FMA per score:
 //     p = exp2(s*c - m*c).  The stabiliser m only moves when the tile max
 //     exceeds it by more than kLazyThreshold (log2 units), so the fp32
