@@ -44,6 +44,8 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_fa_amd", "csrc",
                           "fa_mfma.hip")
+BWD_KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_fa_amd", "csrc",
+                              "fa_bwd_mfma.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -51,8 +53,8 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_source_sha(src: str = KERNEL_SRC) -> str:
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
 def workload_desc(w, causal):
@@ -273,7 +275,7 @@ def cpu_baseline(w, causal, r, budget_s=15.0):
                 seconds=dt)
 
 
-def traffic(kernel_name, workload):
+def traffic(kernel_name, workload, src=KERNEL_SRC):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by what the
     counter reads for a plain copy of known size) from the committed
     rocprofv3 summary for this kernel and workload, if it was taken on the
@@ -283,7 +285,7 @@ def traffic(kernel_name, workload):
     except (OSError, ValueError):
         return None
     rec = t.get(f"{kernel_name} {workload}")
-    if not rec or rec.get("source_sha") != kernel_source_sha():
+    if not rec or rec.get("source_sha") != kernel_source_sha(src):
         return None
     return rec.get("bytes_per_launch")
 
@@ -439,7 +441,8 @@ def main_backward(args, w, causal):
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic(r["kernel"], workload_desc(w, causal) + " backward",
+                               BWD_KERNEL_SRC),
             "kernel": "fa_bwd call: delta, " + r["kernel"] + " (dK/dV), dQ",
             "flops_per_launch": r["flops"],
             "kernel_ms": round(r["kernel_ms"], 5),
