@@ -67,6 +67,9 @@ def _bind(lib):
     lib.oracle_attention_bwd.argtypes = [_F64P] * 8 + [_I64] * 5 + [
         ctypes.c_int, ctypes.c_double]
     lib.oracle_attention_bwd.restype = ctypes.c_int
+    lib.oracle_attention_bwd_win.argtypes = [_F64P] * 8 + [_I64] * 5 + [
+        ctypes.c_int, _I64, _I64, ctypes.c_double]
+    lib.oracle_attention_bwd_win.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -170,11 +173,13 @@ def probs(q, k, causal: bool = False, scale: float | None = None, lib=None):
 
 
 def attention_bwd(q, k, v, dout, causal: bool = False,
-                  scale: float | None = None, lib=None, with_delta=False):
+                  scale: float | None = None, lib=None, with_delta=False,
+                  window=None):
     """fp64 gradients (dq, dk, dv) of the forward for an incoming gradient
     ``dout`` of o (lse takes no gradient).  The plain chain rule through the
     forward definition; the C source states each step.  With ``with_delta``
-    also returns delta [B,H,Lq], delta_i = sum_j p_ij (dout_i . v_j)."""
+    also returns delta [B,H,Lq], delta_i = sum_j p_ij (dout_i . v_j).
+    ``window=(wl, wr)`` as for :func:`attention`."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, H, Lq, Lk, D = _shapes(q, k, v)
     if dout.shape != q.shape:
@@ -185,9 +190,10 @@ def attention_bwd(q, k, v, dout, causal: bool = False,
     dk = np.empty_like(k)
     dv = np.empty_like(v)
     delta = np.empty((B, H, Lq), dtype=np.float64)
-    rc = (lib or load()).oracle_attention_bwd(
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    rc = (lib or load()).oracle_attention_bwd_win(
         _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(delta), B, H, Lq, Lk, D, int(bool(causal)), float(scale))
+        _ptr(delta), B, H, Lq, Lk, D, int(bool(causal)), wl, wr, float(scale))
     if rc != 0:
         raise RuntimeError(f"oracle_attention_bwd failed ({rc})")
     if with_delta:

@@ -267,16 +267,18 @@ int oracle_probs(const double *q, const double *k, double *p_out, int64_t B,
  *   dk_j  = scale * sum_i ds_ij q_i
  *
  * Layouts as for oracle_attention; dout and dq are [B,H,Lq,D], dk and dv
- * [B,H,Lk,D]; delta [B,H,Lq] receives delta_i (may be NULL).  Each head keeps p and ds as dense [Lq, Lk] fp64 matrices.
+ * [B,H,Lk,D]; delta [B,H,Lq] receives delta_i (may be NULL).  wl / wr: the
+ * window of the forward (p is 0 outside it, so are ds and the sums).  Each head keeps p and ds as dense [Lq, Lk] fp64 matrices.
  * Rows are done in parallel (p, ds, dq), then keys (dk, dv), so no sum is
  * shared between threads.  Returns 0, or -1 on a bad shape or allocation
  * failure.
  */
-int oracle_attention_bwd(const double *q, const double *k, const double *v,
-                         const double *dout, double *dq, double *dk,
-                         double *dv, double *delta_out, int64_t B, int64_t H,
-                         int64_t Lq,
-                         int64_t Lk, int64_t D, int causal, double scale)
+int oracle_attention_bwd_win(const double *q, const double *k,
+                             const double *v, const double *dout, double *dq,
+                             double *dk, double *dv, double *delta_out,
+                             int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                             int64_t D, int causal, int64_t wl, int64_t wr,
+                             double scale)
 {
     int64_t bh;
     double *p, *ds;
@@ -298,22 +300,23 @@ int oracle_attention_bwd(const double *q, const double *k, const double *v,
         for (i = 0; i < Lq; ++i) {
             double *pi = p + i * Lk, *dsi = ds + i * Lk;
             const double *gi = gh + i * D;
-            int64_t jend = visible_end(i, Lk, causal, -1), jj, d;
+            int64_t jbeg = visible_begin(i, wl), jj, d;
+            int64_t jend = visible_end(i, Lk, causal, wr);
             double m, l, delta = 0.0;
-            softmax_row(qh + i * D, kh, Lk, D, 0, jend, scale, pi, &m, &l);
+            softmax_row(qh + i * D, kh, Lk, D, jbeg, jend, scale, pi, &m, &l);
             for (jj = 0; jj < Lk; ++jj) dsi[jj] = 0.0;
-            for (jj = 0; jj < jend; ++jj) {
+            for (jj = jbeg; jj < jend; ++jj) {
                 const double *vj = vh + jj * D;
                 double dp = 0.0;
                 for (d = 0; d < D; ++d) dp += gi[d] * vj[d];
                 dsi[jj] = dp;
                 delta += pi[jj] * dp;
             }
-            for (jj = 0; jj < jend; ++jj) dsi[jj] = pi[jj] * (dsi[jj] - delta);
+            for (jj = jbeg; jj < jend; ++jj) dsi[jj] = pi[jj] * (dsi[jj] - delta);
             if (delta_out) delta_out[bh * Lq + i] = delta;
             for (d = 0; d < D; ++d) {
                 double acc = 0.0;
-                for (jj = 0; jj < jend; ++jj) acc += dsi[jj] * kh[jj * D + d];
+                for (jj = jbeg; jj < jend; ++jj) acc += dsi[jj] * kh[jj * D + d];
                 dqh[i * D + d] = scale * acc;
             }
         }
@@ -334,6 +337,17 @@ int oracle_attention_bwd(const double *q, const double *k, const double *v,
     free(p);
     free(ds);
     return 0;
+}
+
+/* The backward without a window. */
+int oracle_attention_bwd(const double *q, const double *k, const double *v,
+                         const double *dout, double *dq, double *dk,
+                         double *dv, double *delta_out, int64_t B, int64_t H,
+                         int64_t Lq, int64_t Lk, int64_t D, int causal,
+                         double scale)
+{
+    return oracle_attention_bwd_win(q, k, v, dout, dq, dk, dv, delta_out, B, H,
+                                    Lq, Lk, D, causal, -1, -1, scale);
 }
 
 /* Threads the OpenMP runtime will use for the calls above. */

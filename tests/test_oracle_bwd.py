@@ -235,8 +235,8 @@ MUTANTS = {
                          "accv += p[ii * Lk + j] * gh[(Lq - 1 - ii) * D + d];"),
     "dk_uses_dout": ("acck += ds[ii * Lk + j] * qh[ii * D + d];",
                      "acck += ds[ii * Lk + j] * gh[ii * D + d];"),
-    "dq_uses_v": ("for (jj = 0; jj < jend; ++jj) acc += dsi[jj] * kh[jj * D + d];",
-                  "for (jj = 0; jj < jend; ++jj) acc += dsi[jj] * vh[jj * D + d];"),
+    "dq_uses_v": ("for (jj = jbeg; jj < jend; ++jj) acc += dsi[jj] * kh[jj * D + d];",
+                  "for (jj = jbeg; jj < jend; ++jj) acc += dsi[jj] * vh[jj * D + d];"),
     "dp_uses_k": ("const double *vj = vh + jj * D;",
                   "const double *vj = kh + jj * D;"),
     "dv_uses_ds": ("accv += p[ii * Lk + j] * gh[ii * D + d];",

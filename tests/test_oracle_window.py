@@ -142,8 +142,68 @@ def pin_rows_entry(lib):
         assert np.array_equal(rl, l.reshape(-1)[ids])
 
 
+def _loss(q, k, v, g, causal, scale, win, lib):
+    o, _ = oracle.attention(q, k, v, causal, scale, lib=lib, window=win)
+    return float(np.sum(o * g))
+
+
+def pin_bwd_finite_differences(lib):
+    """Windowed gradients against central differences of the windowed
+    forward (every entry)."""
+    h = 1e-6
+    for n, ((B, H, Lq, Lk, D), causal, win) in enumerate(
+            [((1, 1, 6, 7, 3), False, (1, 2)), ((1, 1, 7, 7, 2), True, (2, -1)),
+             ((1, 1, 8, 4, 2), False, (1, 0))]):
+        q, k, v = qkv(B, H, Lq, Lk, D, 780 + n)
+        g = rnd((B, H, Lq, D), 790 + n)
+        grads = oracle.attention_bwd(q, k, v, g, causal, 0.6, lib=lib, window=win)
+        for t, (x, gx) in enumerate(zip((q, k, v), grads)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                a = [q.copy(), k.copy(), v.copy()]
+                a[t][idx] += h
+                lp = _loss(*a, g, causal, 0.6, win, lib)
+                a[t][idx] -= 2 * h
+                lm = _loss(*a, g, causal, 0.6, win, lib)
+                num[idx] = (lp - lm) / (2 * h)
+            np.testing.assert_allclose(gx, num, rtol=0, atol=2e-8)
+
+
+def pin_bwd_torch_mask(lib):
+    """torch fp64 autograd of its attention routine with the window as a
+    boolean mask (every row keeps a key here)."""
+    F = torch.nn.functional
+    for n, ((B, H, Lq, Lk, D), causal, (wl, wr)) in enumerate(
+            [((1, 2, 20, 20, 8), False, (3, 2)), ((1, 2, 20, 20, 8), True, (5, -1)),
+             ((2, 1, 17, 29, 4), False, (0, 6))]):
+        q, k, v = qkv(B, H, Lq, Lk, D, 800 + n)
+        g = rnd((B, H, Lq, D), 810 + n)
+        mask = torch.zeros(Lq, Lk, dtype=torch.bool)
+        for i in range(Lq):
+            for j in visible(i, Lk, causal, wl, wr):
+                mask[i, j] = True
+        assert mask.any(1).all()
+        qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.3).backward(
+            torch.tensor(g))
+        grads = oracle.attention_bwd(q, k, v, g, causal, 0.3, lib=lib, window=(wl, wr))
+        for a, b in zip(grads, (qt.grad, kt.grad, vt.grad)):
+            np.testing.assert_allclose(a, b.numpy(), rtol=0, atol=1e-12)
+
+
+def pin_bwd_wide_window_is_plain(lib):
+    q, k, v = qkv(1, 2, 15, 18, 4, 820)
+    g = rnd((1, 2, 15, 4), 821)
+    for causal in (False, True):
+        a = oracle.attention_bwd(q, k, v, g, causal, 0.5, lib=lib)
+        b = oracle.attention_bwd(q, k, v, g, causal, 0.5, lib=lib, window=(40, 40))
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
 PINS = [pin_wide_window_is_plain, pin_right_zero_is_causal, pin_slice, pin_mp_bruteforce,
-        pin_torch_mask, pin_causal_w0, pin_empty_rows, pin_rows_entry]
+        pin_torch_mask, pin_causal_w0, pin_empty_rows, pin_rows_entry,
+        pin_bwd_finite_differences, pin_bwd_torch_mask, pin_bwd_wide_window_is_plain]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -158,6 +218,11 @@ MUTANTS = {
     "left_ignored": ("    if (wl < 0 || i - wl <= 0) return 0;", "    return 0;"),
     "right_ignored": ("if (wr >= 0 && i + wr + 1 < e) e = i + wr + 1;", ""),
     "left_is_right": ("    return i - wl;\n", "    return i - wl > i ? i : i - wl / 2;\n"),
+    "bwd_window_ignored": ("int64_t jbeg = visible_begin(i, wl), jj, d;",
+                           "int64_t jbeg = 0, jj, d;"),
+    "bwd_dq_full_range": ("for (jj = jbeg; jj < jend; ++jj) acc += dsi[jj] * kh[jj * D + d];",
+                          "for (jj = 0; jj < jend; ++jj) acc += (jj < jbeg ? 1.0 : dsi[jj]) "
+                          "* kh[jj * D + d];"),
 }
 
 
