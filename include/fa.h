@@ -178,6 +178,28 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               const int64_t *strides, int causal, int64_t window_left,
               int64_t window_right, float scale, int dtype, void *stream);
 
+/*
+ * fa_bwd_ex -- the gradients of fa_fwd_ex: fa_bwd on strided views and with
+ * the same local window as the forward call that produced o and lse.
+ *
+ * strides  24 int64 values, in elements: (batch, head, row) of q, k, v, o,
+ *          dout, dq, dk, dv, in that order; the same rules as fa_fwd_ex
+ *          (feature dimension contiguous, strides >= 0 and 16-byte
+ *          multiples, dq / dk / dv must not map two elements to one
+ *          address).  lse and delta stay contiguous [B, H, Lq] fp32.
+ * causal, window_left, window_right
+ *          the keep rule of the forward (see fa_fwd_ex); gradients are zero
+ *          for the pairs it drops.
+ * Other arguments, semantics, precision, ownership and errors as fa_bwd.
+ * A call with the contiguous strides and no window runs exactly fa_bwd.
+ */
+int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o,
+              const float *lse, const void *dout, void *dq, void *dk, void *dv,
+              float *delta, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+              int64_t D, const int64_t *strides, int causal,
+              int64_t window_left, int64_t window_right, float scale, int dtype,
+              void *stream);
+
 /* Static text for a status code ("unknown status" for anything else). */
 const char *fa_status_string(int status);
 

@@ -9,11 +9,12 @@ from __future__ import annotations
 
 import math
 
-from ._lib import (FA_BF16, FA_F16, FA_F32, FaError, fa_bwd,
+from ._lib import (FA_BF16, FA_F16, FA_F32, FaError, fa_bwd, fa_bwd_ex,
                    fa_bwd_kernel_name, fa_fwd, fa_fwd_ex, fa_kernel_name,
                    fa_status_string, fa_version, load)
 
-__all__ = ["forward", "backward", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_kernel_name",
+__all__ = ["forward", "backward", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex",
+           "fa_kernel_name",
            "fa_bwd_kernel_name", "fa_status_string", "fa_version", "FaError",
            "dtype_code", "load"]
 
@@ -89,13 +90,15 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None,
 
 def backward(q, k, v, o, lse, dout, causal: bool = False,
              scale: float | None = None, dq=None, dk=None, dv=None,
-             delta=None, stream=None):
+             delta=None, stream=None, window=None):
     """Gradients (dq, dk, dv) of the forward for an incoming ``dout``.
 
-    q, k, v, causal and scale as given to :func:`forward`; o and lse are what
-    it returned; dout is like o.  ``dq``/``dk``/``dv`` and the fp32 [B,H,Lq]
-    workspace ``delta`` may be preallocated.  Raises FaError on a status
-    other than FA_OK.
+    q, k, v, causal, scale and window as given to :func:`forward`; o and lse
+    are what it returned; dout is like o.  Strided views (last dimension
+    contiguous) and a window go through ``fa_bwd_ex``, the rest through
+    ``fa_bwd``.  ``dq``/``dk``/``dv`` (laid out like q/k/v by default) and
+    the fp32 [B,H,Lq] workspace ``delta`` may be preallocated.  Raises
+    FaError on a status other than FA_OK.
     """
     import torch
     load()
@@ -104,8 +107,8 @@ def backward(q, k, v, o, lse, dout, causal: bool = False,
             raise ValueError(f"{name} must be a device tensor")
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, L, D]")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
         if t.dtype != q.dtype:
             raise TypeError("q, k, v, o, dout must share one dtype")
     B, H, Lq, D = q.shape
@@ -126,11 +129,27 @@ def backward(q, k, v, o, lse, dout, causal: bool = False,
         delta = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                dv.data_ptr(), delta.data_ptr(), B, H, Lq, Lk, D,
-                int(bool(causal)), float(scale), dtype_code(q.dtype),
-                stream.cuda_stream)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
+    wl, wr = (-1, -1) if window is None else (
+        -1 if window[0] is None else int(window[0]),
+        -1 if window[1] is None else int(window[1]))
+    tensors = (q, k, v, o, dout, dq, dk, dv)
+    general = (not all(t.is_contiguous() for t in tensors)) or wl >= 0 or wr >= 0
+    if general:
+        strides = [x for t in tensors for x in t.stride()[:3]]
+        rc = fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                       lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                       dv.data_ptr(), delta.data_ptr(), B, H, Lq, Lk, D, strides,
+                       int(bool(causal)), wl, wr, float(scale), dtype_code(q.dtype),
+                       stream.cuda_stream)
+    else:
+        rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                    lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                    dv.data_ptr(), delta.data_ptr(), B, H, Lq, Lk, D,
+                    int(bool(causal)), float(scale), dtype_code(q.dtype),
+                    stream.cuda_stream)
     if rc != 0:
         raise FaError(rc, fa_status_string(rc))
     return dq, dk, dv

@@ -1,6 +1,7 @@
 """ctypes binding of libfa.so: argument marshalling only.
 
 The names match the C ABI in include/fa.h (``fa_fwd``, ``fa_fwd_ex``, ``fa_bwd``,
+``fa_bwd_ex``,
 ``fa_status_string``, ``fa_kernel_name``, ``fa_bwd_kernel_name``,
 ``fa_version``).  Every step of the attention forward and backward runs in
 the HIP kernels; there is no Python or CPU fallback, and loading
@@ -53,6 +54,10 @@ def load(path: str = LIB_PATH):
     lib.fa_bwd.argtypes = [vp] * 10 + [i64] * 5 + [
         ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_ex.argtypes = [vp] * 10 + [i64] * 5 + [
+        ctypes.POINTER(ctypes.c_int64), ctypes.c_int, i64, i64, ctypes.c_float,
+        ctypes.c_int, vp]
+    lib.fa_bwd_ex.restype = ctypes.c_int
     lib.fa_bwd_kernel_name.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                        ctypes.c_float, ctypes.c_int]
     lib.fa_bwd_kernel_name.restype = ctypes.c_char_p
@@ -94,6 +99,19 @@ def fa_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int,
     """Raw call: integer device addresses in, status code out."""
     return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Lq,
                          Lk, D, int(causal), float(scale), int(dtype), stream)
+
+
+def fa_bwd_ex(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int,
+              dk: int, dv: int, delta: int, B: int, H: int, Lq: int, Lk: int,
+              D: int, strides, causal: int, window_left: int,
+              window_right: int, scale: float, dtype: int,
+              stream: int | None) -> int:
+    """Raw call: device addresses, 24 element strides (q, k, v, o, dout, dq,
+    dk, dv; each batch, head, row), window bounds (-1: none)."""
+    arr = (ctypes.c_int64 * 24)(*[int(x) for x in strides]) if strides is not None else None
+    return load().fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Lq,
+                            Lk, D, arr, int(causal), int(window_left),
+                            int(window_right), float(scale), int(dtype), stream)
 
 
 def fa_bwd_kernel_name(B: int, H: int, Lq: int, Lk: int, D: int, causal: int,

@@ -254,9 +254,16 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
     return launch_forward(a);
 }
 
-int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
-           const void *dout, void *dq, void *dk, void *dv, float *delta, int64_t B, int64_t H,
-           int64_t Lq, int64_t Lk, int64_t D, int causal, float scale, int dtype, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by fa_bwd and fa_bwd_ex.  strides: 24
+// values (batch, head, row) of q, k, v, o, dout, dq, dk, dv.
+int bwd_common(const void *q, const void *k, const void *v, const void *o, const float *lse,
+               const void *dout, void *dq, void *dk, void *dv, float *delta, int64_t B,
+               int64_t H, int64_t Lq, int64_t Lk, int64_t D, const int64_t *strides, int causal,
+               int64_t window_left, int64_t window_right, float scale, int dtype, void *stream)
 {
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
         dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || delta == nullptr)
@@ -265,6 +272,16 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     if (rc != FA_OK) return rc;
     // the key-block grid B*H*ceil(Lk/32) must fit a 31-bit launch as well
     if (B * H * ((Lk + 31) / 32) > (int64_t)0x7fffffff) return FA_ERR_SHAPE;
+    const int64_t es = dtype == FA_F32 ? 4 : 2;
+    const int64_t L[8] = {Lq, Lk, Lk, Lq, Lq, Lq, Lk, Lk};
+    for (int i = 0; i < 24; ++i) {
+        if (strides[i] < 0 || strides[i] > ((int64_t)1 << 40)) return FA_ERR_STRIDE;
+        if (i % 3 == 2 && strides[i] > ((int64_t)1 << 24)) return FA_ERR_STRIDE;
+    }
+    for (int t = fa::kDq; t <= fa::kDv; ++t)
+        if (!view_injective(B, H, L[t], D, strides + 3 * t)) return FA_ERR_STRIDE;
+    for (int i = 0; i < 24; ++i)
+        if ((strides[i] * es) % 16 != 0) return FA_ERR_ALIGN;
 
     const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
@@ -274,12 +291,14 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
         ((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(delta)) & 3u) != 0)
         return FA_ERR_ALIGN;
 
-    const int64_t es = dtype == FA_F32 ? 4 : 2;
-    const int64_t nq = B * H * Lq * D * es, nk = B * H * Lk * D * es, nl = B * H * Lq * 4;
+    int64_t n[8];
+    for (int t = 0; t < 8; ++t) n[t] = view_bytes(B, H, L[t], D, strides + 3 * t, es);
+    const int64_t nl = B * H * Lq * 4;
+    // outputs dq, dk, dv, delta against the inputs and each other
     const void *ins[6] = {q, k, v, o, lse, dout};
-    const int64_t in_n[6] = {nq, nk, nk, nq, nl, nq};
+    const int64_t in_n[6] = {n[fa::kQ], n[fa::kK], n[fa::kV], n[fa::kO], nl, n[fa::kDout]};
     void *outs[4] = {dq, dk, dv, delta};
-    const int64_t out_n[4] = {nq, nk, nk, nl};
+    const int64_t out_n[4] = {n[fa::kDq], n[fa::kDk], n[fa::kDv], nl};
     for (int w = 0; w < 4; ++w) {
         for (int r = 0; r < 6; ++r)
             if (overlaps(outs[w], out_n[w], ins[r], in_n[r])) return FA_ERR_ALIAS;
@@ -317,6 +336,14 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     a.scale = scale;
     a.dtype = dtype;
     a.stream = static_cast<hipStream_t>(stream);
+    bool contiguous = true;
+    for (int t = 0; t < 8; ++t) {
+        for (int i = 0; i < 3; ++i) a.st[t][i] = strides[3 * t + i];
+        contiguous = contiguous && is_contiguous(B, H, L[t], D, strides + 3 * t);
+    }
+    a.wl = (window_left < 0 || window_left >= Lq + Lk) ? -1 : (int)window_left;
+    a.wr = (window_right < 0 || window_right >= Lq + Lk) ? -1 : (int)window_right;
+    a.general = !contiguous || a.wl >= 0 || a.wr >= 0;
     fa::MfmaTile unused{};
     bool force_valu = false;
     (void)env_tile(unused, force_valu);
@@ -325,6 +352,33 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
         e = (!force_valu && fa::bwd_mfma_supported(a)) ? fa::bwd_mfma_launch(a)
                                                         : fa::bwd_valu_launch(a);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+           const void *dout, void *dq, void *dk, void *dv, float *delta, int64_t B, int64_t H,
+           int64_t Lq, int64_t Lk, int64_t D, int causal, float scale, int dtype, void *stream)
+{
+    const int64_t sq[3] = {H * Lq * D, Lq * D, D}, sk[3] = {H * Lk * D, Lk * D, D};
+    int64_t st[24];
+    const int64_t *per[8] = {sq, sk, sk, sq, sq, sq, sk, sk};
+    for (int t = 0; t < 8; ++t)
+        for (int i = 0; i < 3; ++i) st[3 * t + i] = per[t][i];
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Lq, Lk, D, st, causal,
+                      -1, -1, scale, dtype, stream);
+}
+
+int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const float *lse,
+              const void *dout, void *dq, void *dk, void *dv, float *delta, int64_t B,
+              int64_t H, int64_t Lq, int64_t Lk, int64_t D, const int64_t *strides, int causal,
+              int64_t window_left, int64_t window_right, float scale, int dtype, void *stream)
+{
+    if (strides == nullptr) return FA_ERR_NULL;
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Lq, Lk, D, strides,
+                      causal, window_left, window_right, scale, dtype, stream);
 }
 
 const char *fa_status_string(int status)

@@ -196,7 +196,28 @@ struct BwdParams {
     uint16_t *dq, *dk, *dv;
     int BH, Lq, Lk, nt;
     float scale, c;  // c = scale * log2(e)
+    // strided / windowed calls only (GEN kernels): heads per batch, window
+    // bounds (-1: none), element strides (batch, head, row) per tensor in
+    // the order q, k, v, o, dout, dq, dk, dv
+    int H, wl, wr;
+    int64_t st[8][3];
 };
+
+// Per-(b, h) element base and row stride of tensor t: the contiguous
+// [B, H, L, D] values unless GEN.
+template <bool GEN, int D>
+__device__ __forceinline__ void tensor_at(const BwdParams &p, int t, int bh, int L,
+                                          int64_t &base, int &row_stride)
+{
+    if constexpr (GEN) {
+        const int b = bh / p.H, h = bh % p.H;
+        base = b * p.st[t][0] + h * p.st[t][1];
+        row_stride = (int)p.st[t][2];
+    } else {
+        base = (int64_t)bh * L * D;
+        row_stride = D;
+    }
+}
 
 // Workgroup id -> (head bh, block t of nt per head).  Hardware places
 // workgroup w on XCD w % 8; consecutive logical ids share an XCD, so one
@@ -274,7 +295,7 @@ __device__ __forceinline__ void store_cols(uint16_t *row_base, int db, int hi, c
 // t+1.  One barrier per step.  Causal tiles a wave cannot see are computed
 // and masked to zero (no branch inside a step).
 // ---------------------------------------------------------------------------
-template <typename Ops, int D, bool CAUSAL, int OCC>
+template <typename Ops, int D, bool CAUSAL, int OCC, bool GEN = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_bwd_dkdv_mfma_kernel(BwdParams p)
 {
@@ -302,15 +323,23 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
     const int kw = k_first + wave * 32;
     const int key = kw + l32;
 
-    const uint16_t *qh = p.q + (int64_t)bh * Lq * D;
-    const uint16_t *gh = p.dout + (int64_t)bh * Lq * D;
+    int64_t q_b, g_b, k_b, v_b, dk_b, dv_b;
+    int q_sl, g_sl, k_sl, v_sl, dk_sl, dv_sl;
+    tensor_at<GEN, D>(p, 0, bh, Lq, q_b, q_sl);
+    tensor_at<GEN, D>(p, 4, bh, Lq, g_b, g_sl);
+    tensor_at<GEN, D>(p, 1, bh, Lk, k_b, k_sl);
+    tensor_at<GEN, D>(p, 2, bh, Lk, v_b, v_sl);
+    tensor_at<GEN, D>(p, 6, bh, Lk, dk_b, dk_sl);
+    tensor_at<GEN, D>(p, 7, bh, Lk, dv_b, dv_sl);
+    const uint16_t *qh = p.q + q_b;
+    const uint16_t *gh = p.dout + g_b;
     // lane l < 32 loads lse of row l of a tile, lane l >= 32 delta of row l-32
     const float *xh = (lane < 32 ? p.lse : p.delta) + (int64_t)bh * Lq;
 
     u32x4 kop[DC], vop[DC];
     {
-        const uint16_t *kr = p.k + ((int64_t)bh * Lk + key) * D + 8 * hi;
-        const uint16_t *vr = p.v + ((int64_t)bh * Lk + key) * D + 8 * hi;
+        const uint16_t *kr = p.k + k_b + (int64_t)key * k_sl + 8 * hi;
+        const uint16_t *vr = p.v + v_b + (int64_t)key * v_sl + 8 * hi;
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
             kop[dc] = key < Lk ? *(const u32x4 *)(kr + dc * 16) : u32x4{0u, 0u, 0u, 0u};
@@ -345,9 +374,9 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
         const uint32_t wb = uniform(smem_base + b + (uint32_t)(wave * 1024));
 #pragma unroll
         for (int n = 0; n < NLD; ++n) {
-            const int64_t o = (int64_t)min(i0 + dm_row[n], Lq - 1) * D + dm_col[n];
-            dma_16B(qh + o, wb + (uint32_t)(n * NW * 1024));
-            dma_16B(gh + o, wb + TILEB + (uint32_t)(n * NW * 1024));
+            const int64_t row = min(i0 + dm_row[n], Lq - 1);
+            dma_16B(qh + row * q_sl + dm_col[n], wb + (uint32_t)(n * NW * 1024));
+            dma_16B(gh + row * g_sl + dm_col[n], wb + TILEB + (uint32_t)(n * NW * 1024));
         }
         dma_4B(xh + min(i0 + l32, Lq - 1), uniform(smem_base + b + 2 * TILEB));
     };
@@ -362,8 +391,15 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
     uint32_t rd_tr[DB][2];
     tr_offsets<D, DB>(lane, rd_tr);
 
-    const int i_begin = CAUSAL ? k_first : 0;
-    const int ntiles = i_begin < Lq ? (Lq - i_begin + BQ - 1) / BQ : 0;
+    // query rows that see some key of the block: [i_begin, i_end)
+    int i_begin = CAUSAL ? k_first : 0;
+    int i_end = Lq;
+    if constexpr (GEN) {
+        if (p.wr >= 0) i_begin = max(i_begin, k_first - p.wr);
+        if (p.wl >= 0) i_end = min(Lq, k_first + BK + p.wl);
+        i_begin = max(i_begin, 0);
+    }
+    const int ntiles = i_begin < i_end ? (i_end - i_begin + BQ - 1) / BQ : 0;
 
     f32x16 s, dp;
     u32x4 pk[2], dsk[2];
@@ -400,14 +436,20 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
             Dl[4 * q4] = d.x; Dl[4 * q4 + 1] = d.y; Dl[4 * q4 + 2] = d.z; Dl[4 * q4 + 3] = d.w;
         }
         // causal: keep key kw + l32 for row i0 + row when row >= lim
-        const int lim = (CAUSAL && i0 < kw + 31) ? kw + l32 - i0 : -1;
-        const int rows = Lq - i0;
+        int lim = (CAUSAL && i0 < kw + 31) ? kw + l32 - i0 : -1;
+        int rows = Lq - i0;
+        if constexpr (GEN) {
+            // rows lim .. rows - 1 (relative to i0) keep this lane's key
+            const int key_abs = kw + l32;
+            if (p.wr >= 0) lim = max(lim, key_abs - p.wr - i0);
+            if (p.wl >= 0) rows = min(rows, key_abs + p.wl + 1 - i0);
+        }
         float pv[16], dsv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float e = exp2_fast(fmaf(s[r], p.c, -L[r] * kLog2e));
-            if (CAUSAL) e = acc_row(r, hi) >= lim ? e : 0.f;
-            if (decltype(tail)::value) e = acc_row(r, hi) < rows ? e : 0.f;
+            if (CAUSAL || GEN) e = acc_row(r, hi) >= lim ? e : 0.f;
+            if (decltype(tail)::value || GEN) e = acc_row(r, hi) < rows ? e : 0.f;
             pv[r] = e;
             dsv[r] = e * (dp[r] - Dl[r]);
         }
@@ -487,8 +529,8 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
     wait_vmcnt<0>();
 
     if (key < Lk) {
-        uint16_t *dkr = p.dk + ((int64_t)bh * Lk + key) * D;
-        uint16_t *dvr = p.dv + ((int64_t)bh * Lk + key) * D;
+        uint16_t *dkr = p.dk + dk_b + (int64_t)key * dk_sl;
+        uint16_t *dvr = p.dv + dv_b + (int64_t)key * dv_sl;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             store_cols<Ops>(dkr, db, hi, dk[db], p.scale);
@@ -500,7 +542,7 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per NW * 32 query rows, 32 per wave; key tiles of 64.
 // ---------------------------------------------------------------------------
-template <typename Ops, int D, bool CAUSAL, int OCC, int NW>
+template <typename Ops, int D, bool CAUSAL, int OCC, int NW, bool GEN = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_bwd_dq_mfma_kernel(BwdParams p)
 {
@@ -527,14 +569,21 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
     const int qrow = qw + l32;
     const bool row_ok = qrow < Lq;
 
-    const uint16_t *kh = p.k + (int64_t)bh * Lk * D;
-    const uint16_t *vh = p.v + (int64_t)bh * Lk * D;
+    int64_t q_b, g_b, k_b, v_b, dq_b;
+    int q_sl, g_sl, k_sl, v_sl, dq_sl;
+    tensor_at<GEN, D>(p, 0, bh, Lq, q_b, q_sl);
+    tensor_at<GEN, D>(p, 4, bh, Lq, g_b, g_sl);
+    tensor_at<GEN, D>(p, 1, bh, Lk, k_b, k_sl);
+    tensor_at<GEN, D>(p, 2, bh, Lk, v_b, v_sl);
+    tensor_at<GEN, D>(p, 5, bh, Lq, dq_b, dq_sl);
+    const uint16_t *kh = p.k + k_b;
+    const uint16_t *vh = p.v + v_b;
 
     // Q^T and dO^T operands (B of S^T = K Q^T and dP^T = V dO^T)
     u32x4 qop[DC], gop[DC];
     {
-        const uint16_t *qr = p.q + ((int64_t)bh * Lq + qrow) * D + 8 * hi;
-        const uint16_t *gr = p.dout + ((int64_t)bh * Lq + qrow) * D + 8 * hi;
+        const uint16_t *qr = p.q + q_b + (int64_t)qrow * q_sl + 8 * hi;
+        const uint16_t *gr = p.dout + g_b + (int64_t)qrow * g_sl + 8 * hi;
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
             qop[dc] = row_ok ? *(const u32x4 *)(qr + dc * 16) : u32x4{0u, 0u, 0u, 0u};
@@ -571,8 +620,14 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
     uint32_t rd_tr[DB][2];
     tr_offsets<D, DB>(lane, rd_tr);
 
-    const int kv_end = CAUSAL ? min(Lk, q_first + BM) : Lk;
-    const int ntiles = (kv_end + BN - 1) / BN;
+    // keys [kv_begin, kv_end) are visible to some row of the block
+    int kv_begin = 0;
+    int kv_end = CAUSAL ? min(Lk, q_first + BM) : Lk;
+    if constexpr (GEN) {
+        if (p.wl >= 0) kv_begin = max(0, q_first - p.wl);
+        if (p.wr >= 0) kv_end = min(kv_end, q_first + BM + p.wr);
+    }
+    const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + BN - 1) / BN : 0;
 
     // Keys past the end fetch the last key (valid memory); their
     // probabilities are masked to zero.
@@ -580,26 +635,26 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
         const uint32_t wb = uniform(smem_base + b + (uint32_t)(wave * 1024));
 #pragma unroll
         for (int n = 0; n < NLD; ++n) {
-            const int64_t o = (int64_t)min(k0 + dm_row[n], Lk - 1) * D + dm_col[n];
-            dma_16B(kh + o, wb + (uint32_t)(n * NW * 1024));
-            dma_16B(vh + o, wb + TILEB + (uint32_t)(n * NW * 1024));
+            const int64_t row = min(k0 + dm_row[n], Lk - 1);
+            dma_16B(kh + row * k_sl + dm_col[n], wb + (uint32_t)(n * NW * 1024));
+            dma_16B(vh + row * v_sl + dm_col[n], wb + TILEB + (uint32_t)(n * NW * 1024));
         }
     };
 
     if (ntiles > 0) {
-        issue(0, 0);
+        issue(kv_begin, 0);
         wait_vmcnt<0>();
         __syncthreads();
     }
     for (int t = 0; t < ntiles; ++t) {
-        const int k0 = t * BN;
+        const int k0 = kv_begin + t * BN;
         const uint8_t *cur = smem + (t & 1) * BUFB;
         const bool more = t + 1 < ntiles;
         if (more) issue(k0 + BN, (uint32_t)(((t + 1) & 1) * BUFB));
         if (!CAUSAL || k0 <= qw + 31) {
             const uint8_t *kt = cur, *vt = cur + TILEB;
             // mask: keys past the diagonal (causal) or past the end
-            const bool need_mask = (CAUSAL && k0 + BN - 1 > qw) || k0 + BN > Lk;
+            const bool need_mask = GEN || (CAUSAL && k0 + BN - 1 > qw) || k0 + BN > Lk;
             u32x4 dsk[KC];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -621,7 +676,11 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
                     float e = exp2_fast(fmaf(s[r], p.c, -lse2));
                     if (need_mask) {
                         const int j = k0 + kb * 32 + acc_row(r, hi);
-                        e = (j < Lk && (!CAUSAL || j <= qrow)) ? e : 0.f;
+                        bool keep = j < Lk && (!CAUSAL || j <= qrow);
+                        if constexpr (GEN)
+                            keep = keep && (p.wr < 0 || j <= qrow + p.wr) &&
+                                   (p.wl < 0 || j >= qrow - p.wl);
+                        e = keep ? e : 0.f;
                     }
                     dsv[r] = e * (dp[r] - dl);
                 }
@@ -645,13 +704,13 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
     }
 
     if (row_ok) {
-        uint16_t *dqr = p.dq + ((int64_t)bh * Lq + qrow) * D;
+        uint16_t *dqr = p.dq + dq_b + (int64_t)qrow * dq_sl;
 #pragma unroll
         for (int db = 0; db < DB; ++db) store_cols<Ops>(dqr, db, hi, dq[db], p.scale);
     }
 }
 
-template <typename Ops, int D, bool CAUSAL>
+template <typename Ops, int D, bool CAUSAL, bool GEN>
 hipError_t launch_t(const BwdArgs &a)
 {
     BwdParams p;
@@ -669,24 +728,36 @@ hipError_t launch_t(const BwdArgs &a)
     p.Lk = (int)a.Lk;
     p.scale = a.scale;
     p.c = a.scale * kLog2e;
+    p.H = (int)a.H;
+    p.wl = a.wl;
+    p.wr = a.wr;
+    for (int t = 0; t < 8; ++t)
+        for (int i = 0; i < 3; ++i) p.st[t][i] = a.st[t][i];
     constexpr int BLK = (kThreads / 64) * 32;
     p.nt = (int)((a.Lk + BLK - 1) / BLK);
-    hipLaunchKernelGGL((fa_bwd_dkdv_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_KV_OCC64 : BWD_KV_OCC128>),
+    hipLaunchKernelGGL((fa_bwd_dkdv_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_KV_OCC64 : BWD_KV_OCC128, GEN>),
                        dim3((unsigned)(p.BH * p.nt)), dim3(kThreads), 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int NWQ = D == 64 ? BWD_Q_NW64 : BWD_Q_NW128;
     p.nt = (int)((a.Lq + NWQ * 32 - 1) / (NWQ * 32));
-    hipLaunchKernelGGL((fa_bwd_dq_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_Q_OCC64 : BWD_Q_OCC128, NWQ>),
+    hipLaunchKernelGGL((fa_bwd_dq_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_Q_OCC64 : BWD_Q_OCC128, NWQ, GEN>),
                        dim3((unsigned)(p.BH * p.nt)), dim3(NWQ * 64), 0, a.stream, p);
     return hipGetLastError();
+}
+
+template <typename Ops, bool GEN>
+hipError_t launch_gen(const BwdArgs &a)
+{
+    if (a.D == 64)
+        return a.causal ? launch_t<Ops, 64, true, GEN>(a) : launch_t<Ops, 64, false, GEN>(a);
+    return a.causal ? launch_t<Ops, 128, true, GEN>(a) : launch_t<Ops, 128, false, GEN>(a);
 }
 
 template <typename Ops>
 hipError_t launch_ops(const BwdArgs &a)
 {
-    if (a.D == 64) return a.causal ? launch_t<Ops, 64, true>(a) : launch_t<Ops, 64, false>(a);
-    return a.causal ? launch_t<Ops, 128, true>(a) : launch_t<Ops, 128, false>(a);
+    return a.general ? launch_gen<Ops, true>(a) : launch_gen<Ops, false>(a);
 }
 
 }  // namespace

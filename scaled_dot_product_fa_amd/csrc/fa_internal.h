@@ -52,7 +52,9 @@ hipError_t mfma_launch_general(const FwdArgs &a);
 const char *valu_kernel_name(const FwdArgs &a);
 hipError_t valu_launch(const FwdArgs &a);
 
-// Arguments of one backward call after validation.
+// Arguments of one backward call after validation.  Element strides
+// (batch, head, row) of q, k, v, o, dout, dq, dk, dv in that order; fa_bwd
+// fills in the contiguous ones.  wl / wr and general as for FwdArgs.
 struct BwdArgs {
     const void *q, *k, *v, *o, *dout;
     const float *lse;
@@ -63,7 +65,11 @@ struct BwdArgs {
     float scale;
     int dtype;
     hipStream_t stream;
+    int64_t st[8][3];
+    int wl, wr;
+    bool general;
 };
+enum { kQ = 0, kK, kV, kO, kDout, kDq, kDk, kDv };
 
 // delta_i = dO_i . O_i into a.delta (any I/O type).
 hipError_t bwd_delta_launch(const BwdArgs &a);

@@ -23,8 +23,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_kernel_name", "fa_fwd",
-                                    "fa_fwd_ex", "fa_kernel_name",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_ex", "fa_bwd_kernel_name",
+                                    "fa_fwd", "fa_fwd_ex", "fa_kernel_name",
                                     "fa_status_string", "fa_version"]
 
 
@@ -246,3 +246,24 @@ def test_ex_output_overlapping_input_rejected():
     assert xcall(o=Q + 16) == 7
     assert xcall(o=K + nbytes - 16) == 7
     assert xcall(lse=O) == 7
+
+
+def test_bwd_ex_validation():
+    B, H, N, D = 1, 2, 128, 64
+    st = contig(B, H, N, D) * 8
+
+    def call(strides):
+        return fa.fa_bwd_ex(Q, K, V, O, L, DO, DQ, DK, DV, DL, B, H, N, N, D,
+                            strides, 0, -1, -1, 0.125, 2, None)
+    assert fa.fa_bwd_ex(Q, K, V, O, L, DO, DQ, DK, DV, DL, B, H, N, N, D, None, 0,
+                        -1, -1, 0.125, 2, None) == 1
+    assert call(st) == 8                       # valid; fake addresses fail last
+    bad = list(st)
+    bad[3 * 5 + 2] = 32                        # dq rows overlap
+    assert call(bad) == 10
+    bad = list(st)
+    bad[3 * 6 + 1] = -64                       # negative dk head stride
+    assert call(bad) == 10
+    bad = list(st)
+    bad[3 * 4 + 2] = 68                        # dout row stride not 16-byte
+    assert call(bad) == 6
