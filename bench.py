@@ -126,8 +126,10 @@ def time_forward(w, causal, steps, warmup, layout="bhld", window=None):
                 q=q, k=k, v=v, o=o.contiguous(), lse=lse, window=window)
 
 
-def time_backward(w, causal, steps, warmup):
-    """Backward: dict with wall ms/step, event ms/call, flops and buffers."""
+def time_backward(w, causal, steps, warmup, layout="bhld", window=None):
+    """Backward: dict with wall ms/step, event ms/call, flops and buffers.
+    layout / window as for time_forward (then fa_bwd_ex; FLOPs 10*D per
+    kept pair)."""
     import torch
     import scaled_dot_product_fa_amd as fa
     from scaled_dot_product_fa_amd import inputs
@@ -135,9 +137,14 @@ def time_backward(w, causal, steps, warmup):
     dev = torch.device("cuda:0")
     q, k, v = inputs.workload_inputs(w)
     g = inputs.make_dout(w.B, w.H, w.Lq, w.D, w.dtype, w.seed)
-    dq_, dk_, dv_, dg = q.to(dev), k.to(dev), v.to(dev), g.to(dev)
+    if layout == "blhd":
+        dq_, dk_, dv_, dg = (t.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+                             for t in (q, k, v, g))
+    else:
+        dq_, dk_, dv_, dg = q.to(dev), k.to(dev), v.to(dev), g.to(dev)
     stream = torch.cuda.current_stream(dev)
-    o, lse = fa.forward(dq_, dk_, dv_, causal=causal, scale=w.scale, stream=stream)
+    o, lse = fa.forward(dq_, dk_, dv_, causal=causal, scale=w.scale, stream=stream,
+                        window=window)
     gq, gk, gv = (torch.empty_like(t) for t in (dq_, dk_, dv_))
     delta = torch.empty_like(lse)
     name = fa.fa_bwd_kernel_name(w.B, w.H, w.Lq, w.Lk, w.D, int(causal), w.scale,
@@ -145,9 +152,16 @@ def time_backward(w, causal, steps, warmup):
     log(f"bench: backward {workload_desc(w, causal)} kernel={name} "
         f"warmup={warmup} steps={steps}")
 
+    general = layout != "bhld" or window is not None
+    if general:
+        name = f"{name} via fa_bwd_ex ({layout}, window {window})"
+        flops = 10.0 * w.B * w.H * w.D * visible_pairs(w.Lq, w.Lk, causal, window)
+    else:
+        flops = 2.5 * w.flops(causal)
+
     def step():
         fa.backward(dq_, dk_, dv_, o, lse, dg, causal=causal, scale=w.scale,
-                    dq=gq, dk=gk, dv=gv, delta=delta, stream=stream)
+                    dq=gq, dk=gk, dv=gv, delta=delta, stream=stream, window=window)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize(dev)
@@ -162,7 +176,7 @@ def time_backward(w, causal, steps, warmup):
     t1 = time.perf_counter()
     return dict(wall_ms=(t1 - t0) * 1e3 / steps,
                 kernel_ms=ev0.elapsed_time(ev1) / steps,
-                flops=2.5 * w.flops(causal), kernel=name,
+                flops=flops, kernel=name, window=window,
                 q=q, k=k, v=v, g=g, dq=gq, dk=gk, dv=gv)
 
 
@@ -180,8 +194,10 @@ def parity_bwd(w, causal, r):
     f64 = lambda t: t.to(torch.float64).numpy()
     (b, h), = bwd_heads(w, 1)[-1:]
     sl = (slice(b, b + 1), slice(h, h + 1))
+    win = r.get("window")
+    win = None if win is None else tuple(win)
     ref = oracle.attention_bwd(f64(r["q"][sl]), f64(r["k"][sl]), f64(r["v"][sl]),
-                               f64(r["g"][sl]), causal, w.scale)
+                               f64(r["g"][sl]), causal, w.scale, window=win)
     out = {"head": [b, h]}
     for name, got, rr in zip(("dq", "dk", "dv"), (r["dq"], r["dk"], r["dv"]), ref):
         out[f"err_{name}"] = float(np.abs(f64(got[sl].cpu()) - rr).max()
@@ -196,13 +212,15 @@ def cpu_baseline_bwd(w, causal, r, budget_s=15.0):
     import torch
     import oracle
     f64 = lambda t: t.to(torch.float64).numpy()
-    per_head = 2.5 * w.flops(causal) / (w.B * w.H)
+    win = r.get("window")
+    win = None if win is None else tuple(win)
+    per_head = r["flops"] / (w.B * w.H)
     done, t_total = 0, 0.0
     for b, h in bwd_heads(w, w.B * w.H):
         sl = (slice(b, b + 1), slice(h, h + 1))
         args = [f64(r[x][sl]) for x in ("q", "k", "v", "g")]
         t0 = time.perf_counter()
-        oracle.attention_bwd(*args, causal, w.scale)
+        oracle.attention_bwd(*args, causal, w.scale, window=win)
         t_total += time.perf_counter() - t0
         done += 1
         if t_total >= budget_s:
@@ -412,7 +430,11 @@ def main():
 def main_backward(args, w, causal):
     steps = args.steps if args.steps != 200 else 40
     warmup = args.warmup if args.warmup != 50 else 10
-    r = time_backward(w, causal, steps, warmup)
+    window = None
+    if args.window is not None:
+        wl, wr = (int(x) for x in args.window.split(","))
+        window = (wl, wr)
+    r = time_backward(w, causal, steps, warmup, args.layout, window)
     tflops = r["flops"] / (r["wall_ms"] * 1e-3) / 1e12
     k_tflops = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
     log(f"bench: backward wall {r['wall_ms']:.4f} ms/step, kernels "
@@ -431,7 +453,9 @@ def main_backward(args, w, causal):
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else w.dtype,
         "data": "synthetic",
-        "config": {"workload": workload_desc(w, causal) + " backward", "B": w.B,
+        "config": {"workload": workload_desc(w, causal) + " backward"
+                   + ("" if args.layout == "bhld" and window is None
+                      else f" {args.layout} window={window}"), "B": w.B,
                    "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "D": w.D, "causal": causal,
                    "scale": w.scale, "io_dtype": w.dtype, "kernel": r["kernel"]},
         "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),

@@ -39,6 +39,11 @@
 // keys and masks (rather than branches around) the few tiles a wave cannot
 // see, so each pipeline step stays one straight-line block.
 //
+// Kernel variants: contiguous tensors (compile-time row strides), strided
+// views (GEN: runtime strides), and strided views with the local window
+// (GEN and WIN: query or key range clipped to the window, window edges
+// masked).
+//
 // Compile-time knobs (defaults are the measured best): waves per SIMD each
 // kernel is register-budgeted for, at D = 64 and D = 128 (BWD_*_OCC*), and
 // whether the dK/dV step pins its MFMA / LDS-read / VALU interleave with
@@ -295,7 +300,8 @@ __device__ __forceinline__ void store_cols(uint16_t *row_base, int db, int hi, c
 // t+1.  One barrier per step.  Causal tiles a wave cannot see are computed
 // and masked to zero (no branch inside a step).
 // ---------------------------------------------------------------------------
-template <typename Ops, int D, bool CAUSAL, int OCC, bool GEN = false>
+// GEN: runtime strides (strided views); WIN: the local window (with GEN).
+template <typename Ops, int D, bool CAUSAL, int OCC, bool GEN = false, bool WIN = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_bwd_dkdv_mfma_kernel(BwdParams p)
 {
@@ -394,7 +400,7 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
     // query rows that see some key of the block: [i_begin, i_end)
     int i_begin = CAUSAL ? k_first : 0;
     int i_end = Lq;
-    if constexpr (GEN) {
+    if constexpr (WIN) {
         if (p.wr >= 0) i_begin = max(i_begin, k_first - p.wr);
         if (p.wl >= 0) i_end = min(Lq, k_first + BK + p.wl);
         i_begin = max(i_begin, 0);
@@ -438,7 +444,7 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
         // causal: keep key kw + l32 for row i0 + row when row >= lim
         int lim = (CAUSAL && i0 < kw + 31) ? kw + l32 - i0 : -1;
         int rows = Lq - i0;
-        if constexpr (GEN) {
+        if constexpr (WIN) {
             // rows lim .. rows - 1 (relative to i0) keep this lane's key
             const int key_abs = kw + l32;
             if (p.wr >= 0) lim = max(lim, key_abs - p.wr - i0);
@@ -448,8 +454,8 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float e = exp2_fast(fmaf(s[r], p.c, -L[r] * kLog2e));
-            if (CAUSAL || GEN) e = acc_row(r, hi) >= lim ? e : 0.f;
-            if (decltype(tail)::value || GEN) e = acc_row(r, hi) < rows ? e : 0.f;
+            if (CAUSAL || WIN) e = acc_row(r, hi) >= lim ? e : 0.f;
+            if (decltype(tail)::value || WIN) e = acc_row(r, hi) < rows ? e : 0.f;
             pv[r] = e;
             dsv[r] = e * (dp[r] - Dl[r]);
         }
@@ -542,7 +548,7 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per NW * 32 query rows, 32 per wave; key tiles of 64.
 // ---------------------------------------------------------------------------
-template <typename Ops, int D, bool CAUSAL, int OCC, int NW, bool GEN = false>
+template <typename Ops, int D, bool CAUSAL, int OCC, int NW, bool GEN = false, bool WIN = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_bwd_dq_mfma_kernel(BwdParams p)
 {
@@ -623,7 +629,7 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
     // keys [kv_begin, kv_end) are visible to some row of the block
     int kv_begin = 0;
     int kv_end = CAUSAL ? min(Lk, q_first + BM) : Lk;
-    if constexpr (GEN) {
+    if constexpr (WIN) {
         if (p.wl >= 0) kv_begin = max(0, q_first - p.wl);
         if (p.wr >= 0) kv_end = min(kv_end, q_first + BM + p.wr);
     }
@@ -654,7 +660,10 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
         if (!CAUSAL || k0 <= qw + 31) {
             const uint8_t *kt = cur, *vt = cur + TILEB;
             // mask: keys past the diagonal (causal) or past the end
-            const bool need_mask = GEN || (CAUSAL && k0 + BN - 1 > qw) || k0 + BN > Lk;
+            bool need_mask = (CAUSAL && k0 + BN - 1 > qw) || k0 + BN > Lk;
+            if constexpr (WIN)
+                need_mask = need_mask || (p.wr >= 0 && k0 + BN - 1 > qw + p.wr) ||
+                            (p.wl >= 0 && k0 < qw + 31 - p.wl);
             u32x4 dsk[KC];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -677,7 +686,7 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
                     if (need_mask) {
                         const int j = k0 + kb * 32 + acc_row(r, hi);
                         bool keep = j < Lk && (!CAUSAL || j <= qrow);
-                        if constexpr (GEN)
+                        if constexpr (WIN)
                             keep = keep && (p.wr < 0 || j <= qrow + p.wr) &&
                                    (p.wl < 0 || j >= qrow - p.wl);
                         e = keep ? e : 0.f;
@@ -710,7 +719,7 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
     }
 }
 
-template <typename Ops, int D, bool CAUSAL, bool GEN>
+template <typename Ops, int D, bool CAUSAL, bool GEN, bool WIN>
 hipError_t launch_t(const BwdArgs &a)
 {
     BwdParams p;
@@ -735,29 +744,33 @@ hipError_t launch_t(const BwdArgs &a)
         for (int i = 0; i < 3; ++i) p.st[t][i] = a.st[t][i];
     constexpr int BLK = (kThreads / 64) * 32;
     p.nt = (int)((a.Lk + BLK - 1) / BLK);
-    hipLaunchKernelGGL((fa_bwd_dkdv_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_KV_OCC64 : BWD_KV_OCC128, GEN>),
+    hipLaunchKernelGGL((fa_bwd_dkdv_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_KV_OCC64 : BWD_KV_OCC128, GEN, WIN>),
                        dim3((unsigned)(p.BH * p.nt)), dim3(kThreads), 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int NWQ = D == 64 ? BWD_Q_NW64 : BWD_Q_NW128;
     p.nt = (int)((a.Lq + NWQ * 32 - 1) / (NWQ * 32));
-    hipLaunchKernelGGL((fa_bwd_dq_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_Q_OCC64 : BWD_Q_OCC128, NWQ, GEN>),
+    hipLaunchKernelGGL((fa_bwd_dq_mfma_kernel<Ops, D, CAUSAL, D == 64 ? BWD_Q_OCC64 : BWD_Q_OCC128, NWQ, GEN, WIN>),
                        dim3((unsigned)(p.BH * p.nt)), dim3(NWQ * 64), 0, a.stream, p);
     return hipGetLastError();
 }
 
-template <typename Ops, bool GEN>
+template <typename Ops, bool GEN, bool WIN>
 hipError_t launch_gen(const BwdArgs &a)
 {
     if (a.D == 64)
-        return a.causal ? launch_t<Ops, 64, true, GEN>(a) : launch_t<Ops, 64, false, GEN>(a);
-    return a.causal ? launch_t<Ops, 128, true, GEN>(a) : launch_t<Ops, 128, false, GEN>(a);
+        return a.causal ? launch_t<Ops, 64, true, GEN, WIN>(a) : launch_t<Ops, 64, false, GEN, WIN>(a);
+    return a.causal ? launch_t<Ops, 128, true, GEN, WIN>(a) : launch_t<Ops, 128, false, GEN, WIN>(a);
 }
 
+// contiguous and unwindowed: compile-time strides, no window code; strided
+// without a window; strided with a window
 template <typename Ops>
 hipError_t launch_ops(const BwdArgs &a)
 {
-    return a.general ? launch_gen<Ops, true>(a) : launch_gen<Ops, false>(a);
+    if (!a.general) return launch_gen<Ops, false, false>(a);
+    if (a.wl < 0 && a.wr < 0) return launch_gen<Ops, true, false>(a);
+    return launch_gen<Ops, true, true>(a);
 }
 
 }  // namespace
