@@ -65,6 +65,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// strided / windowed calls on large grids take the ping-pong kernel (1), or
+// the software-pipelined kernel as on small grids (0)
+#ifndef GENERAL_PP
+#define GENERAL_PP 1
+#endif
+// key tile of the ping-pong kernel with a window at D = 128
+#ifndef PP_WIN_BN
+#define PP_WIN_BN 64
+#endif
 #ifndef PP_LEAD
 #define PP_LEAD 4
 #endif
@@ -931,7 +940,8 @@ void fa_fwd_mfma_dma_kernel(Params p)
 // allows, measured slower: those reads compete with the partner's MFMA
 // phase.)
 // ---------------------------------------------------------------------------
-template <typename Ops, int D, bool CAUSAL, int BN>
+// GEN: strided views (runtime strides); WIN: the local window (with GEN).
+template <typename Ops, int D, bool CAUSAL, int BN, bool GEN = false, bool WIN = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_mfma_pp_kernel(Params p)
 {
@@ -964,9 +974,29 @@ void fa_fwd_mfma_pp_kernel(Params p)
     const int qw = q_first + wave * 32;   // first query row of this wave
     const int qrow = qw + l32;            // this lane's query row
 
-    const uint16_t *qh = p.q + (int64_t)bh * p.Lq * D;
-    const uint16_t *kh = p.k + (int64_t)bh * p.Lk * D;
-    const uint16_t *vh = p.v + (int64_t)bh * p.Lk * D;
+    // per-(b, h) bases and row strides, in elements (GEN: strided views)
+    int64_t qg_base, kg_base, vg_base, og_base;
+    int q_sl, k_sl, v_sl, o_sl;
+    if constexpr (GEN) {
+        const int b = bh / p.H, h = bh % p.H;
+        qg_base = b * p.qs[0] + h * p.qs[1];
+        kg_base = b * p.ks[0] + h * p.ks[1];
+        vg_base = b * p.vs[0] + h * p.vs[1];
+        og_base = b * p.os[0] + h * p.os[1];
+        q_sl = (int)p.qs[2];
+        k_sl = (int)p.ks[2];
+        v_sl = (int)p.vs[2];
+        o_sl = (int)p.os[2];
+    } else {
+        qg_base = (int64_t)bh * p.Lq * D;
+        kg_base = (int64_t)bh * p.Lk * D;
+        vg_base = kg_base;
+        og_base = qg_base;
+        q_sl = k_sl = v_sl = o_sl = D;
+    }
+    const uint16_t *qh = p.q + qg_base;
+    const uint16_t *kh = p.k + kg_base;
+    const uint16_t *vh = p.v + vg_base;
 
     // ---- Q^T operand in VGPRs (rows past Lq read the last row; not stored)
     u32x4 qreg[DC];
@@ -974,11 +1004,19 @@ void fa_fwd_mfma_pp_kernel(Params p)
         const int row = min(qrow, p.Lq - 1);
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
-            qreg[dc] = *reinterpret_cast<const u32x4 *>(qh + (uint32_t)row * D + dc * 16 + hi * 8);
+            qreg[dc] = *reinterpret_cast<const u32x4 *>(
+                qh + (GEN ? (int64_t)row * q_sl : (int64_t)((uint32_t)row * D)) + dc * 16 + hi * 8);
     }
 
-    const int kv_end = CAUSAL ? min(p.Lk, q_first + BM) : p.Lk;
-    const int ntiles = (kv_end + BN - 1) / BN;
+    // keys [kv_begin, kv_end) are visible to some row of the block (WIN:
+    // clipped to the window)
+    int kv_begin = 0;
+    int kv_end = CAUSAL ? min(p.Lk, q_first + BM) : p.Lk;
+    if constexpr (WIN) {
+        if (p.wl >= 0) kv_begin = max(0, q_first - p.wl) / BN * BN;
+        if (p.wr >= 0) kv_end = min(kv_end, q_first + BM + p.wr);
+    }
+    const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + BN - 1) / BN : 0;
 
     // ---- loads: per-lane source offsets (bytes within a tile)
     // (V offset, and K minus V offset: the per-load choice between K and V
@@ -990,8 +1028,8 @@ void fa_fwd_mfma_pp_kernel(Params p)
         const int slot = (r * NW + wave) * 64 + lane;
         const int row = slot / KCH, pc = slot % KCH;
         ld_row[r] = row;
-        ld_v[r] = (uint32_t)(row * D + (pc ^ swz_v<D>(row)) * 8) * 2;
-        ld_kv[r] = (uint32_t)(row * D + (pc ^ swz_k<D>(row)) * 8) * 2 - ld_v[r];
+        ld_v[r] = (uint32_t)(row * v_sl + (pc ^ swz_v<D>(row)) * 8) * 2;
+        ld_kv[r] = (uint32_t)(row * k_sl + (pc ^ swz_k<D>(row)) * 8) * 2 - ld_v[r];
     }
     const uint32_t k_base = lds_addr(k_lds[0]), v_base = lds_addr(v_lds[0]);
     // The loads of one phase, worked out before its straight-line block: the
@@ -1008,15 +1046,16 @@ void fa_fwd_mfma_pp_kernel(Params p)
     };
     auto plan = [&](bool is_k, int tile) {
         LoadPlan pl;
-        const int k0 = min(tile, ntiles - 1) * BN;
-        pl.src = (is_k ? kh : vh) + (int64_t)k0 * D;
+        const int k0 = kv_begin + min(tile, ntiles - 1) * BN;
+        const int sl = is_k ? k_sl : v_sl;
+        pl.src = (is_k ? kh : vh) + (int64_t)k0 * sl;
         pl.dst = (is_k ? k_base : v_base) + (uint32_t)((tile % 3) * TILEB) +
                  (uint32_t)(wave * 1024);
         const int last = p.Lk - 1 - k0;
 #pragma unroll
         for (int r = 0; r < LOADS; ++r)
             pl.off[r] = ld_v[r] + (is_k ? ld_kv[r] : 0u) -
-                        (uint32_t)(max(ld_row[r] - last, 0) * ROWB);
+                        (uint32_t)max(ld_row[r] - last, 0) * (uint32_t)sl * 2u;
         return pl;
     };
     auto issue = [&](const LoadPlan &pl, int r) {
@@ -1127,14 +1166,30 @@ void fa_fwd_mfma_pp_kernel(Params p)
     // Online softmax of tile j in slot t (vector ALU only): mask, row max,
     // lazy rescale, p = exp2(s*c - m*c) rounded to the I/O type, row sum.
     auto softmax = [&](const LoadPlan &pl, int j) {
-        const int k0 = j * BN;
-        if ((k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw)) {
+        const int k0 = kv_begin + j * BN;
+        bool need_mask = (k0 + BN > p.Lk) || (CAUSAL && k0 + BN - 1 > qw);
+        if constexpr (WIN)
+            need_mask = need_mask || (p.wr >= 0 && k0 + BN - 1 > qw + p.wr) ||
+                        (p.wl >= 0 && k0 < qw + 31 - p.wl);
+        if (need_mask) {
+            // element i of block kb holds key k0 + hi*8 + c with the constant
+            // c = kb*32 + (i>>3)*16 + (i&7): kept when lo <= c <= top, the
+            // per-lane bounds folded once (one compare per element)
+            int top = p.Lk - 1 - k0;
+            if (CAUSAL) top = min(top, qrow - k0);
+            int lo = 0;
+            if constexpr (WIN) {
+                if (p.wr >= 0) top = min(top, qrow + p.wr - k0);
+                if (p.wl >= 0) lo = qrow - p.wl - k0 - hi * 8;
+            }
+            top -= hi * 8;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + kb * 32 + (i >> 3) * 16 + hi * 8 + (i & 7);
-                    const bool keep = key < p.Lk && (!CAUSAL || key <= qrow);
+                    const int c = kb * 32 + (i >> 3) * 16 + (i & 7);
+                    bool keep = c <= top;
+                    if constexpr (WIN) keep = keep && c >= lo;
                     st[kb][i] = keep ? st[kb][i] : -INFINITY;
                 }
         }
@@ -1187,71 +1242,76 @@ void fa_fwd_mfma_pp_kernel(Params p)
         if (t != last_slot) __syncthreads();
     };
 
-    // Loads per slot: group 0 runs SM_j in slot 2j+1 (loads K_{j+2}) and
-    // PV_j+QK_{j+1} in slot 2j+2 (loads V_{j+2}); group 1 runs SM_j in slot
-    // 2j+2 (V_{j+2}) and PV_j+QK_{j+1} in slot 2j+3 (K_{j+3}).
-    {
-        const LoadPlan k0p = plan(true, 0), v0p = plan(false, 0), k1p = plan(true, 1);
-#pragma unroll
-        for (int r = 0; r < LOADS; ++r) {
-            issue(k0p, r);
-            issue(v0p, r);
-            issue(k1p, r);
-        }
-    }
-    wait_vmcnt<0>();
-    __syncthreads();
-    int t = 0;
-    if (grp == 1) {   // group 1 starts one slot late, loading its share of V_1
-        const LoadPlan pl = plan(false, 1);
-#pragma unroll
-        for (int r = 0; r < LOADS; ++r) issue(pl, r);
-        slot_end(t);
-        ++t;
-    }
-    {   // S^T of tile 0 (loads V_1 in group 0's slot 0, K_2 in group 1's slot 1)
-        const LoadPlan pl = plan(grp == 1, 1 + grp);
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) qk_mma(k_lds[0], dc, kb);
-#pragma unroll
-        for (int r = 0; r < LOADS; ++r) issue(pl, r);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) __asm__ volatile("" : "+v"(st[kb]));
-        slot_end(t);
-        ++t;
-    }
-    // unrolled by three so that every LDS read address is a constant offset
-    auto tile = [&](int j, const uint8_t *vbuf, const uint8_t *kbuf) {
+    // A block whose rows see no key (possible only with a window) skips the
+    // whole slot sequence, barriers included (the test is the same for every
+    // wave), and stores O = 0, LSE = -inf.
+    if (!WIN || ntiles > 0) {
+        // Loads per slot: group 0 runs SM_j in slot 2j+1 (loads K_{j+2}) and
+        // PV_j+QK_{j+1} in slot 2j+2 (loads V_{j+2}); group 1 runs SM_j in slot
+        // 2j+2 (V_{j+2}) and PV_j+QK_{j+1} in slot 2j+3 (K_{j+3}).
         {
-            const LoadPlan pl = plan(grp == 0, j + 2);
-            softmax(pl, j);
+            const LoadPlan k0p = plan(true, 0), v0p = plan(false, 0), k1p = plan(true, 1);
+#pragma unroll
+            for (int r = 0; r < LOADS; ++r) {
+                issue(k0p, r);
+                issue(v0p, r);
+                issue(k1p, r);
+            }
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+        int t = 0;
+        if (grp == 1) {   // group 1 starts one slot late, loading its share of V_1
+            const LoadPlan pl = plan(false, 1);
+#pragma unroll
+            for (int r = 0; r < LOADS; ++r) issue(pl, r);
             slot_end(t);
             ++t;
         }
-        {
-            const LoadPlan pl = plan(grp == 1, j + 2 + grp);
-            mfma_phase(pl, vbuf, kbuf);
+        {   // S^T of tile 0 (loads V_1 in group 0's slot 0, K_2 in group 1's slot 1)
+            const LoadPlan pl = plan(grp == 1, 1 + grp);
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) qk_mma(k_lds[0], dc, kb);
+#pragma unroll
+            for (int r = 0; r < LOADS; ++r) issue(pl, r);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) __asm__ volatile("" : "+v"(st[kb]));
             slot_end(t);
             ++t;
         }
-    };
-    for (int j = 0; j < ntiles; j += 3) {
-        tile(j, v_lds[0], k_lds[1]);
-        if (j + 1 >= ntiles) break;
-        tile(j + 1, v_lds[1], k_lds[2]);
-        if (j + 2 >= ntiles) break;
-        tile(j + 2, v_lds[2], k_lds[0]);
+        // unrolled by three so that every LDS read address is a constant offset
+        auto tile = [&](int j, const uint8_t *vbuf, const uint8_t *kbuf) {
+            {
+                const LoadPlan pl = plan(grp == 0, j + 2);
+                softmax(pl, j);
+                slot_end(t);
+                ++t;
+            }
+            {
+                const LoadPlan pl = plan(grp == 1, j + 2 + grp);
+                mfma_phase(pl, vbuf, kbuf);
+                slot_end(t);
+                ++t;
+            }
+        };
+        for (int j = 0; j < ntiles; j += 3) {
+            tile(j, v_lds[0], k_lds[1]);
+            if (j + 1 >= ntiles) break;
+            tile(j + 1, v_lds[1], k_lds[2]);
+            if (j + 2 >= ntiles) break;
+            tile(j + 2, v_lds[2], k_lds[0]);
+        }
+        // no load may still be writing LDS when the workgroup ends
+        wait_vmcnt<0>();
     }
-    // no load may still be writing LDS when the workgroup ends
-    wait_vmcnt<0>();
 
     // ---- epilogue: O = acc / l, rounded to nearest even; LSE = m*scale + ln l
     const float l = half_sum(l_part);
     if (qrow < p.Lq) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t *orow = p.o + ((int64_t)bh * p.Lq + qrow) * D;
+        uint16_t *orow = p.o + og_base + (int64_t)qrow * o_sl;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -1266,7 +1326,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
     }
 }
 
-template <typename Ops, int D, bool CAUSAL, int BN>
+template <typename Ops, int D, bool CAUSAL, int BN, bool GEN = false, bool WIN = false>
 hipError_t launch_pp(const FwdArgs &a)
 {
     constexpr int BM = 256;
@@ -1282,9 +1342,18 @@ hipError_t launch_pp(const FwdArgs &a)
     p.ntq = (int)((a.Lq + BM - 1) / BM);
     p.scale = a.scale;
     p.c = a.scale * kLog2e;
+    p.H = (int)a.H;
+    p.wl = a.wl;
+    p.wr = a.wr;
+    for (int i = 0; i < 3; ++i) {
+        p.qs[i] = a.qs[i];
+        p.ks[i] = a.ks[i];
+        p.vs[i] = a.vs[i];
+        p.os[i] = a.os[i];
+    }
     const int64_t nwg = (int64_t)p.BH * p.ntq;
-    hipLaunchKernelGGL((fa_fwd_mfma_pp_kernel<Ops, D, CAUSAL, BN>), dim3((unsigned)nwg), dim3(512),
-                       0, a.stream, p);
+    hipLaunchKernelGGL((fa_fwd_mfma_pp_kernel<Ops, D, CAUSAL, BN, GEN, WIN>), dim3((unsigned)nwg),
+                       dim3(512), 0, a.stream, p);
     return hipGetLastError();
 }
 
@@ -1341,12 +1410,28 @@ hipError_t launch_general_t(const FwdArgs &a)
     return hipGetLastError();
 }
 
-// 8 waves (256 rows per workgroup) once that still gives 512 workgroups,
-// else 4 waves.
+// The ping-pong kernel (96-key tiles at D = 128, 128-key tiles at D = 64)
+// once there are 512 workgroups of 256 rows, as for contiguous calls.
+template <typename Ops, bool WIN>
+hipError_t launch_general_pp(const FwdArgs &a)
+{
+    if (a.D == 64)
+        return a.causal ? launch_pp<Ops, 64, true, 128, true, WIN>(a)
+                        : launch_pp<Ops, 64, false, 128, true, WIN>(a);
+    constexpr int BN = WIN ? PP_WIN_BN : 96;
+    return a.causal ? launch_pp<Ops, 128, true, BN, true, WIN>(a)
+                    : launch_pp<Ops, 128, false, BN, true, WIN>(a);
+}
+
+// Smaller grids: 4 waves of the software-pipelined kernel (128 rows per
+// workgroup, twice as many workgroups).
 template <typename Ops>
 hipError_t launch_general_ops(const FwdArgs &a)
 {
     const bool big = a.B * a.H * ((a.Lq + 255) / 256) >= 512;
+    if (big && GENERAL_PP)
+        return (a.wl >= 0 || a.wr >= 0) ? launch_general_pp<Ops, true>(a)
+                                        : launch_general_pp<Ops, false>(a);
     if (a.D == 64) {
         if (a.causal) return big ? launch_general_t<Ops, 64, true, 8>(a) : launch_general_t<Ops, 64, true, 4>(a);
         return big ? launch_general_t<Ops, 64, false, 8>(a) : launch_general_t<Ops, 64, false, 4>(a);

@@ -179,3 +179,39 @@ def test_workload_blhd_sampled(name, causal, window):
     eo, el = float(np.abs(go - ro).max()), float(np.abs(gl - rl).max())
     say(f"[ex]   rows={ids.numel()} max|dO|={eo:.3e} max|dLSE|={el:.3e}")
     assert eo <= TOL_O[w.dtype] and el <= 1e-3
+
+
+# Grids of 512+ blocks of 256 rows take the ping-pong kernel on the strided /
+# windowed path; checked on sampled rows (all heads sampled by stride).
+PP_CASES = [((4, 32, 1024, 1024, 128, "bf16"), False, None),
+            ((4, 32, 1024, 1024, 128, "bf16"), True, None),
+            ((4, 32, 1024, 1100, 64, "f16"), False, None),
+            ((4, 32, 1024, 1024, 128, "bf16"), True, (64, None)),
+            ((4, 32, 1024, 1024, 128, "bf16"), False, (100, 100)),
+            ((4, 32, 1024, 1100, 64, "f16"), True, (300, None)),
+            # rows past Lk + 16 see no key: whole workgroups skip their tiles
+            ((2, 32, 2048, 512, 128, "bf16"), False, (16, 16))]
+
+
+@pytest.mark.parametrize("case", PP_CASES, ids=lambda c: f"{'x'.join(map(str, c[0]))}_c{int(c[1])}_{c[2]}")
+def test_pingpong_general_sampled(case):
+    (B, H, Lq, Lk, D, dt), causal, window = case
+    assert B * H * ((Lq + 255) // 256) >= 512
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = inputs.make_qkv(B, H, Lq, Lk, D, dt, seed=Lq + Lk + D + B)
+    o, lse = fa.forward(blhd(q), blhd(k), blhd(v), causal=causal, scale=scale, window=window)
+    torch.cuda.synchronize()
+    ids = inputs.sample_rows(B, H, Lq, n_random=12, seed=D, heads=range(0, B * H, 5))
+    win = None if window is None else tuple(-1 if x is None else x for x in window)
+    ro, rl = oracle.attention_rows(to64(q), to64(k), to64(v), ids.numpy(), causal, scale,
+                                   window=win)
+    go = to64(o.contiguous()).reshape(-1, D)[ids.numpy()]
+    gl = lse.cpu().reshape(-1)[ids].double().numpy()
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(gl), empty)
+    assert np.all(go[empty] == 0)
+    eo = float(np.abs(go - ro).max())
+    el = float(np.abs(gl[~empty] - rl[~empty]).max()) if (~empty).any() else 0.0
+    say(f"[ex] pingpong general {case}: rows={ids.numel()} empty={int(empty.sum())} "
+        f"max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O[dt] and el <= 1e-3
