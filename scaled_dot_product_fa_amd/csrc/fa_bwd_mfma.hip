@@ -450,12 +450,15 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
             if (p.wr >= 0) lim = max(lim, key_abs - p.wr - i0);
             if (p.wl >= 0) rows = min(rows, key_abs + p.wl + 1 - i0);
         }
+        // element r is row 8*hi + c(r), c(r) = acc_row(r, 0) a constant
+        lim -= 8 * hi;
+        rows -= 8 * hi;
         float pv[16], dsv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float e = exp2_fast(fmaf(s[r], p.c, -L[r] * kLog2e));
-            if (CAUSAL || WIN) e = acc_row(r, hi) >= lim ? e : 0.f;
-            if (decltype(tail)::value || WIN) e = acc_row(r, hi) < rows ? e : 0.f;
+            if (CAUSAL || WIN) e = acc_row(r, 0) >= lim ? e : 0.f;
+            if (decltype(tail)::value || WIN) e = acc_row(r, 0) < rows ? e : 0.f;
             pv[r] = e;
             dsv[r] = e * (dp[r] - Dl[r]);
         }

@@ -762,20 +762,30 @@ void fa_fwd_mfma_dma_kernel(Params p)
             need_mask = need_mask || (p.wr >= 0 && k0 + BN - 1 > qw + p.wr) ||
                         (p.wl >= 0 && k0 < qw + QB * 32 - 1 - p.wl);
         if (need_mask) {
+            // element i of block kb holds key k0 + hi*8 + c, c = kb*32 +
+            // (i>>3)*16 + (i&7) a constant: kept when lo <= c <= top, with
+            // the bounds folded per lane and row block (one compare each)
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int b = 0; b < QB; ++b) {
+                const int qrow = qw + b * 32 + l32;
+                int top = p.Lk - 1 - k0;
+                if (CAUSAL) top = min(top, qrow - k0);
+                int lo = 0;
+                if constexpr (GEN) {
+                    if (p.wr >= 0) top = min(top, qrow + p.wr - k0);
+                    if (p.wl >= 0) lo = qrow - p.wl - k0 - hi * 8;
+                }
+                top -= hi * 8;
 #pragma unroll
-                for (int b = 0; b < QB; ++b)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int key = k0 + kb * 32 + (i >> 3) * 16 + hi * 8 + (i & 7);
-                        const int qrow = qw + b * 32 + l32;
-                        bool keep = key < p.Lk && (!CAUSAL || key <= qrow);
-                        if constexpr (GEN)
-                            keep = keep && (p.wr < 0 || key <= qrow + p.wr) &&
-                                   (p.wl < 0 || key >= qrow - p.wl);
+                        const int c = kb * 32 + (i >> 3) * 16 + (i & 7);
+                        bool keep = c <= top;
+                        if constexpr (GEN) keep = keep && c >= lo;
                         cur.v[kb][b][i] = keep ? cur.v[kb][b][i] : -INFINITY;
                     }
+            }
         }
         // block A: row maxima of tile j | first half of QK^T for tile j+1
         STile nxt;
