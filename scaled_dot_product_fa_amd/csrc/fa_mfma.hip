@@ -86,6 +86,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // The running max is only raised when it grew by more than this many binary
 // orders of magnitude; until then probabilities may reach 2^kLazyThreshold.
 constexpr float kLazyThreshold = 8.0f;
+// The ping-pong kernel instead keeps its stabiliser while every lane's
+// partial row sum over a tile stays at or below this bound (2^15: any single
+// p is then below the fp16 maximum of 65504).
+constexpr float kPpSumBound = 32768.0f;
 
 struct Bf16Ops {
     static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c)
@@ -1031,30 +1035,37 @@ void fa_fwd_mfma_pp_kernel(Params p)
     // ---- loads: per-lane source offsets (bytes within a tile)
     // (V offset, and K minus V offset: the per-load choice between K and V
     // is then a select against zero, which stays in registers)
+    // A wave's softmax phases always load one tensor and its MFMA phases the
+    // other (group 0: K in softmax phases, V in MFMA phases; group 1 the
+    // reverse), so the whole-tile offsets of both kinds are fixed per wave.
     int ld_row[LOADS];
-    uint32_t ld_v[LOADS], ld_kv[LOADS];
+    uint32_t ld_sm[LOADS], ld_mf[LOADS];
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
         const int slot = (r * NW + wave) * 64 + lane;
         const int row = slot / KCH, pc = slot % KCH;
         ld_row[r] = row;
-        ld_v[r] = (uint32_t)(row * v_sl + (pc ^ swz_v<D>(row)) * 8) * 2;
-        ld_kv[r] = (uint32_t)(row * k_sl + (pc ^ swz_k<D>(row)) * 8) * 2 - ld_v[r];
+        const uint32_t ov = (uint32_t)(row * v_sl + (pc ^ swz_v<D>(row)) * 8) * 2;
+        const uint32_t ok = (uint32_t)(row * k_sl + (pc ^ swz_k<D>(row)) * 8) * 2;
+        ld_sm[r] = grp == 0 ? ok : ov;
+        ld_mf[r] = grp == 0 ? ov : ok;
     }
     const uint32_t k_base = lds_addr(k_lds[0]), v_base = lds_addr(v_lds[0]);
     // The loads of one phase, worked out before its straight-line block: the
     // tile's global base, the LDS destination of this wave's first piece and
-    // the per-lane byte offsets.  Tile t goes to buffer t % 3.  Past the last tile the last tile is fetched again
-    // (into the buffer of the requested tile, which no wave reads any more),
-    // so every slot issues the same loads; rows past the end of the keys
-    // fetch the last valid row (their scores are masked and their V rows get
-    // probability 0).
+    // the per-lane byte offsets (`whole`: those of a tile that lies entirely
+    // below Lk).  Tile t goes to buffer t % 3.  Past the last tile the last
+    // tile is fetched again (into the buffer of the requested tile, which no
+    // wave reads any more), so every slot issues the same loads; rows past
+    // the end of the keys fetch the last valid row (their scores are masked
+    // and their V rows get probability 0).  Only a ragged tile pays for the
+    // per-lane clamp.
     struct LoadPlan {
         const uint16_t *src;
         uint32_t dst;
         uint32_t off[LOADS];
     };
-    auto plan = [&](bool is_k, int tile) {
+    auto plan = [&](bool is_k, int tile, const uint32_t (&whole)[LOADS]) {
         LoadPlan pl;
         const int k0 = kv_begin + min(tile, ntiles - 1) * BN;
         const int sl = is_k ? k_sl : v_sl;
@@ -1063,10 +1074,17 @@ void fa_fwd_mfma_pp_kernel(Params p)
                  (uint32_t)(wave * 1024);
         const int last = p.Lk - 1 - k0;
 #pragma unroll
-        for (int r = 0; r < LOADS; ++r)
-            pl.off[r] = ld_v[r] + (is_k ? ld_kv[r] : 0u) -
-                        (uint32_t)max(ld_row[r] - last, 0) * (uint32_t)sl * 2u;
+        for (int r = 0; r < LOADS; ++r) pl.off[r] = whole[r];
+        if (last < BN - 1) {
+#pragma unroll
+            for (int r = 0; r < LOADS; ++r)
+                pl.off[r] -= (uint32_t)max(ld_row[r] - last, 0) * (uint32_t)sl * 2u;
+        }
         return pl;
+    };
+    // the prologue's loads, of either tensor
+    auto plan_kv = [&](bool is_k, int tile) {
+        return plan(is_k, tile, (grp == 0) == is_k ? ld_sm : ld_mf);
     };
     auto issue = [&](const LoadPlan &pl, int r) {
         dma_16B_sbase(pl.src, pl.off[r], pl.dst + (uint32_t)(r * NW * 1024));
@@ -1089,6 +1107,10 @@ void fa_fwd_mfma_pp_kernel(Params p)
             const int col = db * 32 + 16 * (g & 1) + 4 * (t & 3);   // element
             const int c = col >> 3, within = (col & 7) * 2;
             v_rd[db] = (uint32_t)(row * ROWB + ((c ^ swz_v<D>(row)) * 16) + within);
+            // opaque to the compiler: with the value's known zero bits it
+            // would form every buffer's address with a fresh OR instead of
+            // the read's offset field
+            __asm__ volatile("" : "+v"(v_rd[db]));
         }
     }
 
@@ -1203,14 +1225,22 @@ void fa_fwd_mfma_pp_kernel(Params p)
                     st[kb][i] = keep ? st[kb][i] : -INFINITY;
                 }
         }
-        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        // Stabiliser: the running max is moved to the true max only when it
+        // has to be.  p = exp2(s*c - m*c) is first formed with the current
+        // m; only if some lane's partial row sum exceeds 2^kPpSumBound (so a
+        // p might, and the fp16 range would be at risk) is m raised to the
+        // row max, the accumulator rescaled and the tile's p formed again.
+        // The softmax does not depend on the stabiliser (l and the
+        // accumulator share it), and p stays below 2^kPpSumBound.  Until a
+        // row has seen a key (m = -inf) the max is always taken first.
+        auto to_max = [&]() {
+            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], st[kb][i]);
-        const float mx = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-        const float m_new = fmaxf(m_run, mx);
-        if (__any((m_new - m_run) * c > kLazyThreshold)) {
+                for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], st[kb][i]);
+            const float mx = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+            const float m_new = fmaxf(m_run, mx);
             // m_run = -inf gives alpha = 0 (nothing accumulated yet)
             const float alpha =
                 (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
@@ -1220,25 +1250,39 @@ void fa_fwd_mfma_pp_kernel(Params p)
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        }
-        const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-        float r4[4] = {0.f, 0.f, 0.f, 0.f};
+        };
+        // p of the tile (rounded into pk) and this lane's partial row sum;
+        // the slot's loads are spread over the first pass
+        auto probs = [&](bool loads) {
+            const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+            float r4[4];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
+            for (int kc = 0; kc < KC; ++kc) {
+                if (loads) {
 #pragma unroll
-            for (int r = 0; r < LOADS; ++r)
-                if (kc == r * KC / LOADS) issue(pl, r);
-            const int kb = kc >> 1, h = kc & 1;
-            float e[8];
+                    for (int r = 0; r < LOADS; ++r)
+                        if (kc == r * KC / LOADS) issue(pl, r);
+                }
+                const int kb = kc >> 1, h = kc & 1;
+                float e[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                e[i] = __builtin_amdgcn_exp2f(fmaf(st[kb][h * 8 + i], c, -mc));
-                r4[i & 3] += e[i];
+                for (int i = 0; i < 8; ++i) {
+                    e[i] = __builtin_amdgcn_exp2f(fmaf(st[kb][h * 8 + i], c, -mc));
+                    r4[i & 3] = kc == 0 && i < 4 ? e[i] : r4[i & 3] + e[i];
+                }
+#pragma unroll
+                for (int w = 0; w < 4; ++w) pk[kc][w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
             }
-#pragma unroll
-            for (int w = 0; w < 4; ++w) pk[kc][w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
+            return (r4[0] + r4[1]) + (r4[2] + r4[3]);
+        };
+        const bool unseen = WIN ? __any(m_run == -INFINITY) : j == 0;
+        if (unseen) to_max();
+        float r = probs(true);
+        if (!unseen && __any(r > kPpSumBound)) {   // rare: a second pass
+            to_max();
+            r = probs(false);
         }
-        l_part += (r4[0] + r4[1]) + (r4[2] + r4[3]);
+        l_part += r;
         // P must exist before the barrier
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) __asm__ volatile("" : "+v"(pk[kc]));
@@ -1260,7 +1304,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
         // PV_j+QK_{j+1} in slot 2j+2 (loads V_{j+2}); group 1 runs SM_j in slot
         // 2j+2 (V_{j+2}) and PV_j+QK_{j+1} in slot 2j+3 (K_{j+3}).
         {
-            const LoadPlan k0p = plan(true, 0), v0p = plan(false, 0), k1p = plan(true, 1);
+            const LoadPlan k0p = plan_kv(true, 0), v0p = plan_kv(false, 0), k1p = plan_kv(true, 1);
 #pragma unroll
             for (int r = 0; r < LOADS; ++r) {
                 issue(k0p, r);
@@ -1272,14 +1316,14 @@ void fa_fwd_mfma_pp_kernel(Params p)
         __syncthreads();
         int t = 0;
         if (grp == 1) {   // group 1 starts one slot late, loading its share of V_1
-            const LoadPlan pl = plan(false, 1);
+            const LoadPlan pl = plan(false, 1, ld_sm);
 #pragma unroll
             for (int r = 0; r < LOADS; ++r) issue(pl, r);
             slot_end(t);
             ++t;
         }
         {   // S^T of tile 0 (loads V_1 in group 0's slot 0, K_2 in group 1's slot 1)
-            const LoadPlan pl = plan(grp == 1, 1 + grp);
+            const LoadPlan pl = plan(grp == 1, 1 + grp, ld_mf);
 #pragma unroll
             for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
@@ -1294,13 +1338,13 @@ void fa_fwd_mfma_pp_kernel(Params p)
         // unrolled by three so that every LDS read address is a constant offset
         auto tile = [&](int j, const uint8_t *vbuf, const uint8_t *kbuf) {
             {
-                const LoadPlan pl = plan(grp == 0, j + 2);
+                const LoadPlan pl = plan(grp == 0, j + 2, ld_sm);
                 softmax(pl, j);
                 slot_end(t);
                 ++t;
             }
             {
-                const LoadPlan pl = plan(grp == 1, j + 2 + grp);
+                const LoadPlan pl = plan(grp == 1, j + 2 + grp, ld_mf);
                 mfma_phase(pl, vbuf, kbuf);
                 slot_end(t);
                 ++t;
