@@ -1275,10 +1275,11 @@ void fa_fwd_mfma_pp_kernel(Params p)
             }
             return (r4[0] + r4[1]) + (r4[2] + r4[3]);
         };
+        // (one rescale site: a second branch around the accumulator made the
+        // register allocator copy it on the common path)
         const bool unseen = WIN ? __any(m_run == -INFINITY) : j == 0;
-        if (unseen) to_max();
         float r = probs(true);
-        if (!unseen && __any(r > kPpSumBound)) {   // rare: a second pass
+        if (unseen || __any(r > kPpSumBound)) {   // rare: a second pass
             to_max();
             r = probs(false);
         }
