@@ -147,6 +147,34 @@ def test_pingpong_tile_counts(Lk, tile, D, dt, monkeypatch):
         check_full(q, k, v, causal, 0.09, dt, f"pingpong {tile} Lk={Lk}")
 
 
+# The ping-pong kernel keeps its stabiliser until a lane's partial row sum
+# over a tile passes 2^15, then moves it to the row max and forms the tile's
+# probabilities again.  Scores here climb across the keys so that this
+# happens (a) through one key whose probability alone would overflow fp16
+# and (b) through a whole tile of moderately larger scores, with quiet tiles
+# between and a ragged last tile.
+def _climbing_scores(Lq, Lk, D, dt, seed):
+    g = torch.Generator().manual_seed(seed)
+    t = torch.zeros(Lk)
+    t[96:] = 40.0                 # every probability about 2^5: no rescale
+    t[200] = 200.0                # one key about 2^26 above the stabiliser
+    t[288:384] = 300.0            # a tile of keys about 2^13 above it
+    t[384:] = 295.0
+    q = 1.0 + 0.05 * torch.randn(1, 2, Lq, D, generator=g)
+    k = t.view(1, 1, Lk, 1) / D + 0.02 * torch.randn(1, 2, Lk, D, generator=g)
+    v = torch.randn(1, 2, Lk, D, generator=g)
+    return (x.to(DT[dt]) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("tile,D,dt", [("8x1x96x2x3", 128, "bf16"), ("8x1x96x2x3", 128, "f16"),
+                                       ("8x1x128x2x3", 64, "f16"), ("8x1x64x2x3", 128, "bf16")])
+def test_pingpong_stabiliser_moves(tile, D, dt, monkeypatch):
+    monkeypatch.setenv("FA_TILE", tile)
+    for Lq, Lk, causal in ((300, 700, False), (700, 700, True)):
+        q, k, v = _climbing_scores(Lq, Lk, D, dt, seed=D + Lq)
+        check_full(q, k, v, causal, 0.09, dt, f"pingpong stabiliser {tile}")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5, 1e-3])
 def test_scale_values(scale):
     q, k, v = inputs.make_qkv(1, 2, 150, 200, 64, "bf16", seed=11)
