@@ -1540,6 +1540,11 @@ hipError_t launch_tile_dma(const FwdArgs &a, const MfmaTile &t)
         return launch_dma<Ops, D, CAUSAL, 4, 1, 64, 2>(a);
     if (t.nw == 4 && t.qb == 2 && t.bn == 64 && t.occ == 1)
         return launch_dma<Ops, D, CAUSAL, 4, 2, 64, 1>(a);
+    // narrow workgroups (64 and 32 query rows) spread small grids over more CUs
+    if (t.nw == 2 && t.qb == 1 && t.bn == 64 && t.occ == 1)
+        return launch_dma<Ops, D, CAUSAL, 2, 1, 64, 1>(a);
+    if (t.nw == 1 && t.qb == 1 && t.bn == 64 && t.occ == 1)
+        return launch_dma<Ops, D, CAUSAL, 1, 1, 64, 1>(a);
     return hipErrorInvalidConfiguration;
 }
 

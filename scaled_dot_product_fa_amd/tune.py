@@ -31,8 +31,10 @@ TABLE_INC = os.path.join(PKG, "csrc", "fa_tiles.inc")
 # "NWxQBxBNxOCCxPIPE" strings the library accepts (see fa_internal.h)
 TILES = {
     64: ["8x1x128x2x3", "8x1x64x2x3", "8x1x64x2x2", "4x1x64x2x2", "4x2x64x1x2",
+         "2x1x64x1x2", "1x1x64x1x2",
          "8x1x64x2x0", "4x1x64x2x0", "4x1x64x1x0", "4x2x64x1x0"],
     128: ["8x1x96x2x3", "8x1x64x2x3", "8x1x64x2x2", "4x1x64x2x2", "4x2x64x1x2",
+          "2x1x64x1x2", "1x1x64x1x2",
           "8x1x64x2x0", "4x1x64x2x0", "4x1x64x1x0", "4x2x64x1x0"],
 }
 

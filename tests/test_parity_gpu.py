@@ -118,7 +118,8 @@ def test_ragged(shape, causal):
 
 
 @pytest.mark.parametrize("tile", ["4x1x64x1x0", "4x1x64x2x0", "8x1x64x2x0", "4x2x64x1x0",
-                                  "8x1x64x2x2", "4x1x64x2x2", "4x2x64x1x2", "8x1x64x2x3", "8x1x128x2x3",
+                                  "8x1x64x2x2", "4x1x64x2x2", "4x2x64x1x2", "2x1x64x1x2", "1x1x64x1x2",
+                                  "8x1x64x2x3", "8x1x128x2x3",
                                   "8x1x96x2x3", "valu"])
 @pytest.mark.parametrize("D,dt", [(64, "bf16"), (128, "f16")])
 def test_tile_variants(tile, D, dt, monkeypatch):
