@@ -682,20 +682,28 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
                     s = Ops::mma(*(const u32x4 *)(kt + bo + rd_row[dc]), qop[dc], s);
                     dp = Ops::mma(*(const u32x4 *)(vt + bo + rd_row[dc]), gop[dc], dp);
                 }
-                float dsv[16];
+                // exponent arguments; masked ones become -inf (probability
+                // 0, for any scale including 0).  Only tiles that cross the
+                // diagonal, the window or the end of the keys take the mask
+                // block (a separate block: inside the element loop the
+                // compiler turned the uniform test into selects on every tile)
+                float x[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float e = exp2_fast(fmaf(s[r], p.c, -lse2));
-                    if (need_mask) {
+                for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], p.c, -lse2);
+                if (need_mask) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
                         const int j = k0 + kb * 32 + acc_row(r, hi);
                         bool keep = j < Lk && (!CAUSAL || j <= qrow);
                         if constexpr (WIN)
                             keep = keep && (p.wr < 0 || j <= qrow + p.wr) &&
                                    (p.wl < 0 || j >= qrow - p.wl);
-                        e = keep ? e : 0.f;
+                        x[r] = keep ? x[r] : -INFINITY;
                     }
-                    dsv[r] = e * (dp[r] - dl);
                 }
+                float dsv[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dsv[r] = exp2_fast(x[r]) * (dp[r] - dl);
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
