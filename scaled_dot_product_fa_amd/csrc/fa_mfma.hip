@@ -1032,9 +1032,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
     }
     const int ntiles = kv_end > kv_begin ? (kv_end - kv_begin + BN - 1) / BN : 0;
 
-    // ---- loads: per-lane source offsets (bytes within a tile)
-    // (V offset, and K minus V offset: the per-load choice between K and V
-    // is then a select against zero, which stays in registers)
+    // ---- loads: per-lane source offsets (bytes within a tile).
     // A wave's softmax phases always load one tensor and its MFMA phases the
     // other (group 0: K in softmax phases, V in MFMA phases; group 1 the
     // reverse), so the whole-tile offsets of both kinds are fixed per wave.
@@ -1227,12 +1225,13 @@ void fa_fwd_mfma_pp_kernel(Params p)
         }
         // Stabiliser: the running max is moved to the true max only when it
         // has to be.  p = exp2(s*c - m*c) is first formed with the current
-        // m; only if some lane's partial row sum exceeds 2^kPpSumBound (so a
-        // p might, and the fp16 range would be at risk) is m raised to the
-        // row max, the accumulator rescaled and the tile's p formed again.
-        // The softmax does not depend on the stabiliser (l and the
-        // accumulator share it), and p stays below 2^kPpSumBound.  Until a
-        // row has seen a key (m = -inf) the max is always taken first.
+        // m; only if some lane's partial row sum exceeds kPpSumBound = 2^15
+        // (so a single p might, and the fp16 range would be at risk) is m
+        // raised to the row max, the accumulator rescaled and the tile's p
+        // formed again.  The softmax does not depend on the stabiliser (l and
+        // the accumulator share it), and p stays at or below 2^15.  Until a
+        // row has seen a key (m = -inf) the max is always taken (first pass
+        // discarded).
         auto to_max = [&]() {
             float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -1540,7 +1539,8 @@ hipError_t launch_tile_dma(const FwdArgs &a, const MfmaTile &t)
         return launch_dma<Ops, D, CAUSAL, 4, 1, 64, 2>(a);
     if (t.nw == 4 && t.qb == 2 && t.bn == 64 && t.occ == 1)
         return launch_dma<Ops, D, CAUSAL, 4, 2, 64, 1>(a);
-    // narrow workgroups (64 and 32 query rows) spread small grids over more CUs
+    // narrow workgroups (64 and 32 query rows): more workgroups on small
+    // grids; in the tile sweep they lose to the 4-wave tile (latency bound)
     if (t.nw == 2 && t.qb == 1 && t.bn == 64 && t.occ == 1)
         return launch_dma<Ops, D, CAUSAL, 2, 1, 64, 1>(a);
     if (t.nw == 1 && t.qb == 1 && t.bn == 64 && t.occ == 1)
