@@ -215,3 +215,33 @@ def test_pingpong_general_sampled(case):
     say(f"[ex] pingpong general {case}: rows={ids.numel()} empty={int(empty.sum())} "
         f"max|dO|={eo:.3e} max|dLSE|={el:.3e}")
     assert eo <= TOL_O[dt] and el <= 1e-3
+
+
+# The windowed ping-pong kernel with scores that climb across the keys, so
+# that its stabiliser moves (one key whose probability alone would pass the
+# fp16 range, then a whole tile of larger scores) while some waves have not
+# yet seen a key of their window.
+def test_pingpong_window_stabiliser_moves():
+    B, H, L, D, dt = 1, 128, 1024, 128, "bf16"
+    assert B * H * ((L + 255) // 256) >= 512
+    g = torch.Generator().manual_seed(11)
+    t = torch.zeros(L)
+    t[96:] = 40.0
+    t[200] = 200.0
+    t[288:384] = 300.0
+    t[384:] = 295.0
+    q = (1.0 + 0.05 * torch.randn(B, H, L, D, generator=g)).to(torch.bfloat16)
+    k = (t.view(1, 1, L, 1) / D + 0.02 * torch.randn(B, H, L, D, generator=g)).to(torch.bfloat16)
+    v = torch.randn(B, H, L, D, generator=g).to(torch.bfloat16)
+    scale = 0.09
+    o, lse = fa.forward(blhd(q), blhd(k), blhd(v), causal=True, scale=scale, window=(256, None))
+    torch.cuda.synchronize()
+    ids = inputs.sample_rows(B, H, L, n_random=16, seed=3, heads=range(0, B * H, 9))
+    ro, rl = oracle.attention_rows(to64(q), to64(k), to64(v), ids.numpy(), True, scale,
+                                   window=(256, -1))
+    go = to64(o.contiguous()).reshape(-1, D)[ids.numpy()]
+    gl = lse.cpu().reshape(-1)[ids].double().numpy()
+    eo, el = float(np.abs(go - ro).max()), float(np.abs(gl - rl).max())
+    say(f"[ex] pingpong window stabiliser: rows={ids.numel()} max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert np.isfinite(go).all() and np.isfinite(gl).all()
+    assert eo <= TOL_O[dt] and el <= 1e-3
