@@ -176,6 +176,38 @@ def test_pingpong_stabiliser_moves(tile, D, dt, monkeypatch):
         check_full(q, k, v, causal, 0.09, dt, f"pingpong stabiliser {tile}")
 
 
+# Full-size shapes beyond the five workloads, served by the large-grid
+# kernels: D=64 over 16K keys (128-key ping-pong tiles; with the peaky keys
+# the stabiliser moves many times along a row) and fp16 at D=128 (64- and
+# 96-key ping-pong tiles); sampled rows against the oracle.
+EXTRA_FULL = [((1, 32, 16384, 16384, 64, "bf16"), False),
+              ((1, 32, 16384, 16384, 64, "f16"), True),
+              ((4, 16, 4096, 4096, 128, "f16"), False),
+              ((4, 16, 4096, 4096, 128, "f16"), True)]
+
+
+@pytest.mark.parametrize("shape,causal", EXTRA_FULL,
+                         ids=[f"{'x'.join(map(str, s))}-{'causal' if c else 'noncausal'}"
+                              for s, c in EXTRA_FULL])
+def test_large_grid_sampled(shape, causal):
+    B, H, Lq, Lk, D, dt = shape
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = inputs.make_qkv(B, H, Lq, Lk, D, dt, seed=Lq + D + int(causal),
+                              peaky_frac=0.01, peaky_factor=8.0)
+    say(f"[parity] large grid {shape} causal={causal} kernel="
+        f"{fa.fa_kernel_name(B, H, Lq, Lk, D, int(causal), scale, fa.dtype_code(q.dtype))}")
+    o, lse = gpu_forward(q, k, v, causal, scale)
+    ids = inputs.sample_rows(B, H, Lq, n_random=16, seed=D, tile=128, heads=range(0, B * H, 3))
+    ro, rl = oracle.attention_rows(to64(q), to64(k), to64(v), ids.numpy(), causal, scale)
+    go = to64(o.reshape(-1, D)[ids])
+    gl = lse.reshape(-1)[ids].double().numpy()
+    eo, el = np.abs(go - ro).max(), np.abs(gl - rl).max()
+    say(f"[parity]   rows={ids.numel()} max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert np.isfinite(go).all() and np.isfinite(gl).all()
+    assert eo <= TOL_O[dt], eo
+    assert el <= TOL_LSE, el
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5, 1e-3])
 def test_scale_values(scale):
     q, k, v = inputs.make_qkv(1, 2, 150, 200, 64, "bf16", seed=11)
