@@ -118,6 +118,16 @@ struct F16Ops {
     }
 };
 
+// When the ping-pong kernel does move its stabiliser, bf16 rows place it this
+// many binary orders above the row max, so that later, larger keys fit under
+// the bound without another move (bf16 has the exponent range; fp16 would
+// push small probabilities into its subnormals, so fp16 rows use the max).
+template <typename Ops>
+constexpr float pp_headroom()
+{
+    return std::is_same<Ops, Bf16Ops>::value ? 8.0f : 0.0f;
+}
+
 // Exchange between lane l and lane l ^ 32, combined with op.  With both
 // operands equal, v_permlane32_swap leaves one copy of each half in each
 // result, so op(r0, r1) is op(x[l % 32], x[l % 32 + 32]) in every lane.
@@ -1119,6 +1129,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
     float m_run = -INFINITY, l_part = 0.f;
     const float c = p.c;
+    const float head = pp_headroom<Ops>() / c;   // in score units (c > 0 here)
 
     f32x16 st[KB];    // S^T of the tile whose softmax runs next
     u32x4 pk[KC];     // P^T (I/O type) of the tile whose PV runs next
@@ -1228,10 +1239,10 @@ void fa_fwd_mfma_pp_kernel(Params p)
         // m; only if some lane's partial row sum exceeds kPpSumBound = 2^15
         // (so a single p might, and the fp16 range would be at risk) is m
         // raised to the row max, the accumulator rescaled and the tile's p
-        // formed again.  The softmax does not depend on the stabiliser (l and
-        // the accumulator share it), and p stays at or below 2^15.  Until a
-        // row has seen a key (m = -inf) the max is always taken (first pass
-        // discarded).
+        // formed again (bf16: pp_headroom orders above the max).  The softmax
+        // does not depend on the stabiliser (l and the accumulator share it),
+        // and p stays at or below 2^15.  Until a row has seen a key (m =
+        // -inf) the max is always taken (first pass discarded).
         auto to_max = [&]() {
             float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -1239,7 +1250,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], st[kb][i]);
             const float mx = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-            const float m_new = fmaxf(m_run, mx);
+            const float m_new = fmaxf(m_run, mx + head);
             // m_run = -inf gives alpha = 0 (nothing accumulated yet)
             const float alpha =
                 (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
