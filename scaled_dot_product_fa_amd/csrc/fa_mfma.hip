@@ -120,12 +120,14 @@ struct F16Ops {
 
 // When the ping-pong kernel does move its stabiliser, bf16 rows place it this
 // many binary orders above the row max, so that later, larger keys fit under
-// the bound without another move (bf16 has the exponent range; fp16 would
-// push small probabilities into its subnormals, so fp16 rows use the max).
+// the bound without another move.  bf16 has the exponent range: a p that is
+// 24 + 100 orders below the max is still a normal number, and anything
+// smaller is negligible.  fp16 would push small probabilities into its
+// subnormals, so fp16 rows use the max itself.
 template <typename Ops>
 constexpr float pp_headroom()
 {
-    return std::is_same<Ops, Bf16Ops>::value ? 8.0f : 0.0f;
+    return std::is_same<Ops, Bf16Ops>::value ? 24.0f : 0.0f;
 }
 
 // Exchange between lane l and lane l ^ 32, combined with op.  With both
