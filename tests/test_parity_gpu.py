@@ -324,3 +324,53 @@ def test_native_library_is_the_one_loaded():
     hip = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
     assert len(hip) == 1, hip   # one HIP runtime shared with torch
     assert lib is not None
+
+
+# Seeded random shapes across kernels, masks and tiles: Lq, Lk drawn from
+# 1..700 (ragged against every tile size), D in {64, 128}, bf16/fp16, causal
+# or not, sometimes a window, and a forced tile for the MFMA kernels (the
+# ping-pong tiles only where they are built).  Every output element against
+# the oracle.
+def _random_cases(n=32, seed=2024):
+    g = np.random.default_rng(seed)
+    tiles = {64: ["8x1x128x2x3", "8x1x64x2x3", "4x1x64x2x2", "8x1x64x2x2", "4x2x64x1x2", None],
+             128: ["8x1x96x2x3", "8x1x64x2x3", "4x1x64x2x2", "8x1x64x2x2", "4x2x64x1x2", None]}
+    cases = []
+    for i in range(n):
+        D = int(g.choice([64, 128]))
+        dt = str(g.choice(["bf16", "f16"]))
+        Lq, Lk = int(g.integers(1, 701)), int(g.integers(1, 701))
+        causal = bool(g.integers(0, 2))
+        window = None
+        if g.random() < 0.3:
+            window = (int(g.integers(0, 300)), int(g.integers(-1, 50)))
+        tile = tiles[D][int(g.integers(0, len(tiles[D])))]
+        cases.append((i, 1 + int(g.integers(0, 2)), 1 + int(g.integers(0, 3)), Lq, Lk, D, dt,
+                      causal, window, tile))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"r{c[0]}")
+def test_random_shapes(case, monkeypatch):
+    i, B, H, Lq, Lk, D, dt, causal, window, tile = case
+    if tile is not None and window is None:
+        monkeypatch.setenv("FA_TILE", tile)
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = inputs.make_qkv(B, H, Lq, Lk, D, dt, seed=1000 + i)
+    say(f"[parity] random r{i}: B={B} H={H} Lq={Lq} Lk={Lk} D={D} {dt} causal={causal} "
+        f"window={window} tile={tile if window is None else 'auto'}")
+    dq, dk, dv = (t.cuda() for t in (q, k, v))
+    o, lse = fa.forward(dq, dk, dv, causal=causal, scale=scale,
+                        window=None if window is None else
+                        (window[0], None if window[1] < 0 else window[1]))
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(to64(q), to64(k), to64(v), causal, scale, window=window)
+    go, gl = to64(o.cpu()), lse.cpu().double().numpy()
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(gl), empty)
+    assert np.all(go[empty] == 0)
+    eo = float(np.abs(go - ro).max())
+    el = float(np.abs(gl[~empty] - rl[~empty]).max()) if (~empty).any() else 0.0
+    say(f"[parity]   max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O[dt], eo
+    assert el <= TOL_LSE, el
