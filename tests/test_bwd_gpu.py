@@ -179,3 +179,25 @@ def test_workload_sampled_heads(name, mode, heads):
         say(f"[bwd]   head ({b},{h}) " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
         for n, e in errs.items():
             assert e <= TOL[w.dtype], (n, e)
+
+
+# Seeded random shapes for the backward: Lq, Lk drawn from 1..600, D in
+# {64, 128}, bf16/fp16/fp32, causal or not, scales from the usual 1/sqrt(D)
+# to a negative one; all gradients against the oracle's.
+def _random_bwd_cases(n=20, seed=77):
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        D = int(g.choice([64, 128]))
+        dt = str(g.choice(["bf16", "f16", "f32"], p=[0.45, 0.45, 0.1]))
+        scale = float(g.choice([1.0 / math.sqrt(D), 0.05, -0.07]))
+        cases.append((i, 1 + int(g.integers(0, 2)), 1 + int(g.integers(0, 2)),
+                      int(g.integers(1, 601)), int(g.integers(1, 601)), D, dt,
+                      bool(g.integers(0, 2)), scale))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_bwd_cases(), ids=lambda c: f"r{c[0]}")
+def test_random_shapes_bwd(case):
+    i, B, H, Lq, Lk, D, dt, causal, scale = case
+    check(B, H, Lq, Lk, D, dt, causal, scale=scale, seed=500 + i, label=f"random r{i}")
