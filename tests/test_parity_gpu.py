@@ -215,6 +215,19 @@ def test_scale_values(scale):
         check_full(q, k, v, causal, scale, "bf16", f"scale={scale}")
 
 
+# Very large scales: scores span hundreds of binary orders, so the ping-pong
+# kernel's stabiliser moves on many tiles and most probabilities underflow.
+@pytest.mark.parametrize("scale", [4.0, 20.0])
+@pytest.mark.parametrize("tile,D,dt", [("8x1x96x2x3", 128, "bf16"), ("8x1x64x2x3", 128, "f16"),
+                                       ("8x1x128x2x3", 64, "bf16"), (None, 64, "f16")])
+def test_large_scales(scale, tile, D, dt, monkeypatch):
+    if tile is not None:
+        monkeypatch.setenv("FA_TILE", tile)
+    q, k, v = inputs.make_qkv(1, 2, 300, 700, D, dt, seed=int(scale) + D)
+    for causal in (False, True):
+        check_full(q, k, v, causal, scale, dt, f"scale={scale} tile={tile}")
+
+
 # ------------------------------------------------------------ closed forms
 
 @pytest.mark.parametrize("Lk", [4000, 4001, 4096])
