@@ -40,9 +40,11 @@
 //   * exp2 is used with c = scale*log2(e) folded into one FMA per score:
 //     p = exp2(s*c - m*c).  The stabiliser m only moves when the tile max
 //     exceeds it by more than kLazyThreshold (log2 units), so the fp32
-//     accumulator is rescaled rarely; the softmax is unchanged by the choice
-//     of stabiliser (both l and the accumulator use the same one) and p stays
-//     below 2^kLazyThreshold.
+//     accumulator is rescaled rarely.  In exact arithmetic the softmax does
+//     not depend on the stabiliser (l and the accumulator share it); in
+//     finite precision it does unless l sums the same rounded p as the P.V
+//     product (see Bf16Ops), which the bf16 kernels do.  p stays below
+//     2^kLazyThreshold.
 //   * Workgroup ids are remapped so one head's query blocks run on one XCD
 //     (shared L2), and causal grids start with the longest blocks.
 
@@ -50,6 +52,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <set>
+#include <string>
 #include <type_traits>
 
 #include "fa_internal.h"
@@ -91,7 +96,19 @@ constexpr float kLazyThreshold = 8.0f;
 // p is then below the fp16 maximum of 65504).
 constexpr float kPpSumBound = 32768.0f;
 
+// Normalisation in finite precision.  O's numerator sums the probabilities
+// as rounded for the P.V product, so O is a convex combination of V rows
+// only if its denominator sums those same rounded values.  A denominator of
+// unrounded fp32 p leaves the rounding error of a dominant key (relative
+// u = 2^-8 in bf16) in the numerator alone, a bias of up to u*|v| that comes
+// on top of O's own rounding.  So bf16 kernels keep two row sums: the
+// rounded one (summed with v_dot2 against 1.0, one op per packed pair)
+// divides O, and the fp32 one gives the row statistic m + ln l, which the
+// rounded sum would move by up to u on rows with few keys.  In fp16
+// (u = 2^-11) the same bias is below 2^-11 * max|v|, so fp16 kernels divide
+// by the fp32 sum.
 struct Bf16Ops {
+    static constexpr bool kRoundedNorm = true;
     static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -103,9 +120,17 @@ struct Bf16Ops {
         bf16x2 r = {(__bf16)x, (__bf16)y};
         return __builtin_bit_cast(uint32_t, r);
     }
+    // s + both values of a packed pair (as rounded)
+    static __device__ __forceinline__ float add2(uint32_t x, float s)
+    {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
+                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), s,
+                                               false);
+    }
 };
 
 struct F16Ops {
+    static constexpr bool kRoundedNorm = false;
     static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(
@@ -115,6 +140,11 @@ struct F16Ops {
     {
         f16x2 r = {(_Float16)x, (_Float16)y};
         return __builtin_bit_cast(uint32_t, r);
+    }
+    static __device__ __forceinline__ float add2(uint32_t x, float s)
+    {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x),
+                                      __builtin_bit_cast(f16x2, 0x3c003c00u), s, false);
     }
 };
 
@@ -248,11 +278,14 @@ void fa_fwd_mfma_kernel(Params p)
         for (int b = 0; b < QB; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[db][b][i] = 0.f;
-    float m_run[QB], l_part[QB];
+    // l_part: fp32 row sum (for the row statistic); l_rnd: sum of the
+    // rounded p (divides O; bf16 only, see Bf16Ops)
+    float m_run[QB], l_part[QB], l_rnd[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
         m_run[b] = -INFINITY;
         l_part[b] = 0.f;
+        l_rnd[b] = 0.f;
     }
 
     const int kv_end = CAUSAL ? min(p.Lk, q_first + BM) : p.Lk;
@@ -407,13 +440,14 @@ void fa_fwd_mfma_kernel(Params p)
                                             : __builtin_amdgcn_exp2f((m_run[b] - m_new) * c);
                     m_run[b] = m_new;
                     l_part[b] *= alpha;
+                    if constexpr (Ops::kRoundedNorm) l_rnd[b] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db)
 #pragma unroll
                         for (int i = 0; i < 16; ++i) oacc[db][b][i] *= alpha;
                 }
                 const float mc = (m_run[b] == -INFINITY) ? 0.f : m_run[b] * c;
-                float rs = 0.f;
+                float rs = 0.f, rr = 0.f;
 #pragma unroll
                 for (int kb_i = 0; kb_i < KB; ++kb_i) {
                     float e[16];
@@ -426,12 +460,15 @@ void fa_fwd_mfma_kernel(Params p)
                     for (int h = 0; h < 2; ++h) {
                         u32x4 x;
 #pragma unroll
-                        for (int w = 0; w < 4; ++w)
+                        for (int w = 0; w < 4; ++w) {
                             x[w] = Ops::pack2(e[h * 8 + 2 * w], e[h * 8 + 2 * w + 1]);
+                            if constexpr (Ops::kRoundedNorm) rr = Ops::add2(x[w], rr);
+                        }
                         pk[kb_i * 2 + h][b] = x;
                     }
                 }
                 l_part[b] += rs;
+                if constexpr (Ops::kRoundedNorm) l_rnd[b] += rr;
             }
 
             // ---- O^T += V^T P^T
@@ -457,9 +494,10 @@ void fa_fwd_mfma_kernel(Params p)
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
         const float l = half_sum(l_part[b]);
+        const float ln = Ops::kRoundedNorm ? half_sum(l_rnd[b]) : l;
         const int row = qw + b * 32 + l32;
         if (row < p.Lq) {
-            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const float inv = ln > 0.f ? 1.f / ln : 0.f;
             uint16_t *orow = p.o + ((int64_t)bh * p.Lq + row) * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -698,11 +736,14 @@ void fa_fwd_mfma_dma_kernel(Params p)
         for (int b = 0; b < QB; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[db][b][i] = 0.f;
-    float m_run[QB], l_part[QB];
+    // l_part: fp32 row sum (for the row statistic); l_rnd: sum of the
+    // rounded p (divides O; bf16 only, see Bf16Ops)
+    float m_run[QB], l_part[QB], l_rnd[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
         m_run[b] = -INFINITY;
         l_part[b] = 0.f;
+        l_rnd[b] = 0.f;
     }
     const float c = p.c;
 
@@ -840,6 +881,7 @@ void fa_fwd_mfma_dma_kernel(Params p)
                                         : __builtin_amdgcn_exp2f((m_run[b] - m_new[b]) * c);
                 m_run[b] = m_new[b];
                 l_part[b] *= alpha;
+                if constexpr (Ops::kRoundedNorm) l_rnd[b] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -851,12 +893,13 @@ void fa_fwd_mfma_dma_kernel(Params p)
         // the exponentials of the later chunks under the PV MFMAs of the
         // earlier ones.  That keeps MFMA and VALU work balanced inside each
         // phase.
-        float mc[QB], r4[QB][4];
+        float mc[QB], r4[QB][4], rr[QB][2];
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
             mc[b] = (m_run[b] == -INFINITY) ? 0.f : m_run[b] * c;
 #pragma unroll
             for (int w = 0; w < 4; ++w) r4[b][w] = 0.f;
+            rr[b][0] = rr[b][1] = 0.f;
         }
         auto make_p = [&](int kc, int b) {
             const int kb = kc >> 1, h = kc & 1;
@@ -868,7 +911,10 @@ void fa_fwd_mfma_dma_kernel(Params p)
             }
             u32x4 x;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) x[w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
+            for (int w = 0; w < 4; ++w) {
+                x[w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
+                if constexpr (Ops::kRoundedNorm) rr[b][w & 1] = Ops::add2(x[w], rr[b][w & 1]);
+            }
             return x;
         };
         u32x4 pk[KC][QB];
@@ -895,7 +941,10 @@ void fa_fwd_mfma_dma_kernel(Params p)
             }
         }
 #pragma unroll
-        for (int b = 0; b < QB; ++b) l_part[b] += (r4[b][0] + r4[b][1]) + (r4[b][2] + r4[b][3]);
+        for (int b = 0; b < QB; ++b) {
+            l_part[b] += (r4[b][0] + r4[b][1]) + (r4[b][2] + r4[b][3]);
+            if constexpr (Ops::kRoundedNorm) l_rnd[b] += rr[b][0] + rr[b][1];
+        }
         // K reads two MFMA groups ahead; the transposed V reads stay ahead of
         // the PV MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);                 // LDS read
@@ -925,9 +974,10 @@ void fa_fwd_mfma_dma_kernel(Params p)
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
         const float l = half_sum(l_part[b]);
+        const float ln = Ops::kRoundedNorm ? half_sum(l_rnd[b]) : l;
         const int row = qw + b * 32 + l32;
         if (row < p.Lq) {
-            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const float inv = ln > 0.f ? 1.f / ln : 0.f;
             uint16_t *orow = p.o + o_base + (int64_t)row * o_sl;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -1129,7 +1179,9 @@ void fa_fwd_mfma_pp_kernel(Params p)
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    float m_run = -INFINITY, l_part = 0.f;
+    // l_part: fp32 row sum (for the row statistic); l_rnd: sum of the
+    // rounded p (divides O; bf16 only, see Bf16Ops)
+    float m_run = -INFINITY, l_part = 0.f, l_rnd = 0.f;
     const float c = p.c;
     const float head = pp_headroom<Ops>() / c;   // in score units (c > 0 here)
 
@@ -1241,10 +1293,12 @@ void fa_fwd_mfma_pp_kernel(Params p)
         // m; only if some lane's partial row sum exceeds kPpSumBound = 2^15
         // (so a single p might, and the fp16 range would be at risk) is m
         // raised to the row max, the accumulator rescaled and the tile's p
-        // formed again (bf16: pp_headroom orders above the max).  The softmax
-        // does not depend on the stabiliser (l and the accumulator share it),
-        // and p stays at or below 2^15.  Until a row has seen a key (m =
-        // -inf) the max is always taken (first pass discarded).
+        // formed again (bf16: pp_headroom orders above the max).  In exact
+        // arithmetic the softmax does not depend on the stabiliser (l and
+        // the accumulator share it); in bf16 the largest p is then not a
+        // power of two, so O is divided by the sum of the rounded p (see
+        // Bf16Ops).  p stays at or below 2^15.  Until a row has seen a key
+        // (m = -inf) the max is always taken (first pass discarded).
         auto to_max = [&]() {
             float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -1258,16 +1312,19 @@ void fa_fwd_mfma_pp_kernel(Params p)
                 (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
             m_run = m_new;
             l_part *= alpha;
+            if constexpr (Ops::kRoundedNorm) l_rnd *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
         };
-        // p of the tile (rounded into pk) and this lane's partial row sum;
-        // the slot's loads are spread over the first pass
+        // p of the tile (rounded into pk) and this lane's partial row sums
+        // (fp32 in the result, rounded p in rr); the slot's loads are spread
+        // over the first pass
+        float rr;
         auto probs = [&](bool loads) {
             const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-            float r4[4];
+            float r4[4], r2[2];
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 if (loads) {
@@ -1283,8 +1340,13 @@ void fa_fwd_mfma_pp_kernel(Params p)
                     r4[i & 3] = kc == 0 && i < 4 ? e[i] : r4[i & 3] + e[i];
                 }
 #pragma unroll
-                for (int w = 0; w < 4; ++w) pk[kc][w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
+                for (int w = 0; w < 4; ++w) {
+                    pk[kc][w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
+                    if constexpr (Ops::kRoundedNorm)
+                        r2[w & 1] = Ops::add2(pk[kc][w], kc == 0 && w < 2 ? 0.f : r2[w & 1]);
+                }
             }
+            if constexpr (Ops::kRoundedNorm) rr = r2[0] + r2[1];
             return (r4[0] + r4[1]) + (r4[2] + r4[3]);
         };
         // (one rescale site: a second branch around the accumulator made the
@@ -1296,6 +1358,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
             r = probs(false);
         }
         l_part += r;
+        if constexpr (Ops::kRoundedNorm) l_rnd += rr;
         // P must exist before the barrier
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) __asm__ volatile("" : "+v"(pk[kc]));
@@ -1376,8 +1439,9 @@ void fa_fwd_mfma_pp_kernel(Params p)
 
     // ---- epilogue: O = acc / l, rounded to nearest even; LSE = m*scale + ln l
     const float l = half_sum(l_part);
+    const float ln = Ops::kRoundedNorm ? half_sum(l_rnd) : l;
     if (qrow < p.Lq) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float inv = ln > 0.f ? 1.f / ln : 0.f;
         uint16_t *orow = p.o + og_base + (int64_t)qrow * o_sl;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -1627,16 +1691,29 @@ MfmaTile mfma_choose_tile(const FwdArgs &a)
     return MfmaTile{4, 1, 64, 2, 2};
 }
 
+// Interned copy of a kernel label: the returned pointer stays valid for the
+// life of the process and is the same for equal labels.
+static const char *intern_name(const char *s)
+{
+    static std::mutex mu;
+    static std::set<std::string> names;
+    std::lock_guard<std::mutex> lock(mu);
+    return names.insert(s).first->c_str();
+}
+
+// "fa_fwd_mfma_<dtype>_d<D>[_causal]_<family><waves>w[<QB>q]_bn<BN>", with
+// family pp (ping-pong), pipe (software-pipelined, LDS DMA) or reg (K/V
+// staged through registers; "_occ<waves per SIMD>" appended).
 const char *mfma_kernel_name(const FwdArgs &a, const MfmaTile &t)
 {
-    (void)t;
-    static const char *names[2][2][2] = {
-        {{"fa_fwd_mfma_f16_d64", "fa_fwd_mfma_f16_d64_causal"},
-         {"fa_fwd_mfma_f16_d128", "fa_fwd_mfma_f16_d128_causal"}},
-        {{"fa_fwd_mfma_bf16_d64", "fa_fwd_mfma_bf16_d64_causal"},
-         {"fa_fwd_mfma_bf16_d128", "fa_fwd_mfma_bf16_d128_causal"}},
-    };
-    return names[a.dtype == 2][a.D == 128][a.causal ? 1 : 0];
+    const char *fam = t.pipe == 3 ? "pp" : t.pipe == 2 ? "pipe" : "reg";
+    char buf[96];
+    int n = snprintf(buf, sizeof buf, "fa_fwd_mfma_%s_d%d%s_%s%dw", a.dtype == 2 ? "bf16" : "f16",
+                     (int)a.D, a.causal ? "_causal" : "", fam, t.nw);
+    if (t.qb > 1) n += snprintf(buf + n, sizeof buf - n, "%dq", t.qb);
+    n += snprintf(buf + n, sizeof buf - n, "_bn%d", t.bn);
+    if (t.pipe == 0) snprintf(buf + n, sizeof buf - n, "_occ%d", t.occ);
+    return intern_name(buf);
 }
 
 hipError_t mfma_launch(const FwdArgs &a, const MfmaTile &t)
@@ -1644,15 +1721,17 @@ hipError_t mfma_launch(const FwdArgs &a, const MfmaTile &t)
     return a.dtype == 2 ? launch_ops<Bf16Ops>(a, t) : launch_ops<F16Ops>(a, t);
 }
 
+// As mfma_kernel_name, for the strided / windowed kernels that
+// mfma_launch_general picks ("_strided", "_window" when a window is given).
 const char *mfma_general_kernel_name(const FwdArgs &a)
 {
-    static const char *names[2][2][2] = {
-        {{"fa_fwd_mfma_f16_d64_strided", "fa_fwd_mfma_f16_d64_causal_strided"},
-         {"fa_fwd_mfma_f16_d128_strided", "fa_fwd_mfma_f16_d128_causal_strided"}},
-        {{"fa_fwd_mfma_bf16_d64_strided", "fa_fwd_mfma_bf16_d64_causal_strided"},
-         {"fa_fwd_mfma_bf16_d128_strided", "fa_fwd_mfma_bf16_d128_causal_strided"}},
-    };
-    return names[a.dtype == 2][a.D == 128][a.causal ? 1 : 0];
+    const bool big = a.B * a.H * ((a.Lq + 255) / 256) >= 512;
+    const bool win = a.wl >= 0 || a.wr >= 0;
+    MfmaTile t{big ? 8 : 4, 1, 64, 2, 2};
+    if (big && GENERAL_PP) t = MfmaTile{8, 1, a.D == 64 ? 128 : (win ? PP_WIN_BN : 96), 2, 3};
+    char buf[128];
+    snprintf(buf, sizeof buf, "%s_strided%s", mfma_kernel_name(a, t), win ? "_window" : "");
+    return intern_name(buf);
 }
 
 hipError_t mfma_launch_general(const FwdArgs &a)

@@ -104,12 +104,16 @@ def test_non_device_pointers_rejected_without_gpu():
 
 def test_kernel_selection():
     # bf16/fp16 with a positive scale run on MFMA, everything else on VALU
+    # (labels name the kernel family and its tile: pp = ping-pong, pipe =
+    # software-pipelined; waves per workgroup; keys per tile)
     assert fa.fa_kernel_name(4, 16, 4096, 4096, 128, 0, 0.088, 2) == \
-        "fa_fwd_mfma_bf16_d128"
+        "fa_fwd_mfma_bf16_d128_pp8w_bn64"
     assert fa.fa_kernel_name(1, 32, 16384, 16384, 128, 1, 0.088, 2) == \
-        "fa_fwd_mfma_bf16_d128_causal"
+        "fa_fwd_mfma_bf16_d128_causal_pp8w_bn96"
     assert fa.fa_kernel_name(8, 16, 1024, 4000, 64, 0, 0.125, 1) == \
-        "fa_fwd_mfma_f16_d64"
+        "fa_fwd_mfma_f16_d64_pp8w_bn128"
+    assert fa.fa_kernel_name(2, 8, 1024, 1024, 64, 1, 0.125, 2) == \
+        "fa_fwd_mfma_bf16_d64_causal_pipe4w_bn64"
     assert fa.fa_kernel_name(1, 2, 128, 128, 64, 1, 0.125, 0) == \
         "fa_fwd_valu_f32_d64_causal"
     assert fa.fa_kernel_name(1, 2, 128, 128, 64, 0, 0.0, 2) == \
