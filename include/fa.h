@@ -45,8 +45,9 @@ enum fa_status {
     FA_ERR_ALIAS = 7,     /* an output overlaps an input or another output */
     FA_ERR_POINTER = 8,   /* a pointer is not device memory of this device */
     FA_ERR_LAUNCH = 9,    /* the HIP runtime rejected the kernel launch */
-    FA_ERR_STRIDE = 10    /* fa_fwd_ex: a stride is negative or too large, or o
+    FA_ERR_STRIDE = 10,   /* fa_fwd_ex: a stride is negative or too large, or o
                              is a view whose elements overlap */
+    FA_ERR_SCRATCH = 11   /* fa_bwd_noalloc: B*H*Lq > FA_NOALLOC_MAX_ROWS */
 };
 
 /* Size limits checked by fa_fwd (FA_ERR_SHAPE past them). */
@@ -199,6 +200,29 @@ int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o,
               int64_t D, const int64_t *strides, int causal,
               int64_t window_left, int64_t window_right, float scale, int dtype,
               void *stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The same gradients, kernels and precision as fa_bwd, but the
+ * per-row statistic delta lives in a fixed scratch array inside the library
+ * instead of a caller workspace, so there is no delta argument.  Nothing is
+ * allocated: no hipMalloc, hipFree or allocating library call.
+ *
+ * Limit: B*H*Lq <= FA_NOALLOC_MAX_ROWS (2^21 rows, an 8 MiB fp32 array that
+ * each GPU the library runs on holds until the process ends); larger calls
+ * return FA_ERR_SCRATCH before anything is enqueued.
+ * Sharing: every call on one GPU uses that GPU's one array, so calls that
+ * overlap in time on one GPU (different streams or threads) race on it and
+ * must be serialised by the caller.  Every call writes the rows it reads
+ * before reading them, so nothing needs clearing between calls.
+ * Arguments, ownership and the other errors as fa_bwd (contiguous tensors).
+ */
+#define FA_NOALLOC_MAX_ROWS (1LL << 21)
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                   const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                   int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                   int causal, float scale, int dtype, void *stream);
 
 /* Static text for a status code ("unknown status" for anything else). */
 const char *fa_status_string(int status);

@@ -9,11 +9,12 @@ from __future__ import annotations
 
 import math
 
-from ._lib import (FA_BF16, FA_F16, FA_F32, FaError, fa_bwd, fa_bwd_ex,
-                   fa_bwd_kernel_name, fa_fwd, fa_fwd_ex, fa_kernel_name,
-                   fa_status_string, fa_version, load)
+from ._lib import (FA_BF16, FA_F16, FA_F32, FA_NOALLOC_MAX_ROWS, FaError,
+                   fa_bwd, fa_bwd_ex, fa_bwd_kernel_name, fa_bwd_noalloc, fa_fwd,
+                   fa_fwd_ex, fa_kernel_name, fa_status_string, fa_version, load)
 
 __all__ = ["forward", "backward", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex",
+           "fa_bwd_noalloc", "FA_NOALLOC_MAX_ROWS",
            "fa_kernel_name",
            "fa_bwd_kernel_name", "fa_status_string", "fa_version", "FaError",
            "dtype_code", "load"]

@@ -1,7 +1,7 @@
 """ctypes binding of libfa.so: argument marshalling only.
 
 The names match the C ABI in include/fa.h (``fa_fwd``, ``fa_fwd_ex``, ``fa_bwd``,
-``fa_bwd_ex``,
+``fa_bwd_ex``, ``fa_bwd_noalloc``,
 ``fa_status_string``, ``fa_kernel_name``, ``fa_bwd_kernel_name``,
 ``fa_version``).  Every step of the attention forward and backward runs in
 the HIP kernels; there is no Python or CPU fallback, and loading
@@ -20,7 +20,9 @@ STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM",
     4: "FA_ERR_DTYPE", 5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS",
     8: "FA_ERR_POINTER", 9: "FA_ERR_LAUNCH", 10: "FA_ERR_STRIDE",
+    11: "FA_ERR_SCRATCH",
 }
+FA_NOALLOC_MAX_ROWS = 1 << 21
 
 _lib = None
 
@@ -58,6 +60,9 @@ def load(path: str = LIB_PATH):
         ctypes.POINTER(ctypes.c_int64), ctypes.c_int, i64, i64, ctypes.c_float,
         ctypes.c_int, vp]
     lib.fa_bwd_ex.restype = ctypes.c_int
+    lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [i64] * 5 + [
+        ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+    lib.fa_bwd_noalloc.restype = ctypes.c_int
     lib.fa_bwd_kernel_name.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                        ctypes.c_float, ctypes.c_int]
     lib.fa_bwd_kernel_name.restype = ctypes.c_char_p
@@ -112,6 +117,17 @@ def fa_bwd_ex(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int,
     return load().fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Lq,
                             Lk, D, arr, int(causal), int(window_left),
                             int(window_right), float(scale), int(dtype), stream)
+
+
+def fa_bwd_noalloc(q: int, k: int, v: int, o: int, lse: int, dout: int,
+                   dq: int, dk: int, dv: int, B: int, H: int, Lq: int, Lk: int,
+                   D: int, causal: int, scale: float, dtype: int,
+                   stream: int | None) -> int:
+    """Raw call of fa_bwd without a delta workspace (the library's fixed
+    scratch holds it; B*H*Lq <= FA_NOALLOC_MAX_ROWS)."""
+    return load().fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq,
+                                 Lk, D, int(causal), float(scale), int(dtype),
+                                 stream)
 
 
 def fa_bwd_kernel_name(B: int, H: int, Lq: int, Lk: int, D: int, causal: int,

@@ -12,10 +12,41 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
+
 #include "fa.h"
 #include "fa_internal.h"
 
+// Fixed device scratch of fa_bwd_noalloc: the per-row statistic delta (fp32
+// [B, H, Lq]) of up to FA_NOALLOC_MAX_ROWS rows, 8 MiB.  Each device holds
+// its own copy until the process ends.  In host code this name is not a
+// device address: kernels and copies take the per-device address that
+// noalloc_scratch() obtains with hipGetSymbolAddress.
+static __device__ __align__(256) float scratch[FA_NOALLOC_MAX_ROWS];
+
 namespace {
+
+// Device address of `scratch` on `device` (the current device), looked up
+// once per device and kept.  FA_OK, or FA_ERR_LAUNCH if the runtime cannot
+// resolve the symbol.
+int noalloc_scratch(int device, float **out)
+{
+    static std::mutex mu;
+    static std::map<int, float *> ptrs;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = ptrs.find(device);
+    if (it == ptrs.end()) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return FA_ERR_LAUNCH;
+        }
+        it = ptrs.emplace(device, static_cast<float *>(p)).first;
+    }
+    *out = it->second;
+    return FA_OK;
+}
 
 bool overlaps(const void *a, int64_t an, const void *b, int64_t bn)
 {
@@ -258,12 +289,15 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
 
 namespace {
 
-// Validation and launch shared by fa_bwd and fa_bwd_ex.  strides: 24
-// values (batch, head, row) of q, k, v, o, dout, dq, dk, dv.
+// Validation and launch shared by fa_bwd, fa_bwd_ex and fa_bwd_noalloc.
+// strides: 24 values (batch, head, row) of q, k, v, o, dout, dq, dk, dv.
+// delta_internal: delta is the library's own scratch (not a caller buffer,
+// so it is not checked as one).
 int bwd_common(const void *q, const void *k, const void *v, const void *o, const float *lse,
                const void *dout, void *dq, void *dk, void *dv, float *delta, int64_t B,
                int64_t H, int64_t Lq, int64_t Lk, int64_t D, const int64_t *strides, int causal,
-               int64_t window_left, int64_t window_right, float scale, int dtype, void *stream)
+               int64_t window_left, int64_t window_right, float scale, int dtype, void *stream,
+               bool delta_internal = false)
 {
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
         dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || delta == nullptr)
@@ -313,7 +347,7 @@ int bwd_common(const void *q, const void *k, const void *v, const void *o, const
     }
     for (int r = 0; r < 6; ++r)
         if (!is_device_ptr(ins[r], device)) return FA_ERR_POINTER;
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < (delta_internal ? 3 : 4); ++w)
         if (!is_device_ptr(outs[w], device)) return FA_ERR_POINTER;
 
     fa::BwdArgs a;
@@ -371,6 +405,34 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
                       -1, -1, scale, dtype, stream);
 }
 
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                   const float *lse, const void *dout, void *dq, void *dk, void *dv, int64_t B,
+                   int64_t H, int64_t Lq, int64_t Lk, int64_t D, int causal, float scale,
+                   int dtype, void *stream)
+{
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
+        dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+        return FA_ERR_NULL;
+    int rc = check_args(B, H, Lq, Lk, D, scale, dtype);
+    if (rc != FA_OK) return rc;
+    if (B * H * Lq > FA_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH;
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) {
+        (void)hipGetLastError();
+        return FA_ERR_POINTER;
+    }
+    float *ws = nullptr;
+    rc = noalloc_scratch(device, &ws);
+    if (rc != FA_OK) return rc;
+    const int64_t sq[3] = {H * Lq * D, Lq * D, D}, sk[3] = {H * Lk * D, Lk * D, D};
+    int64_t st[24];
+    const int64_t *per[8] = {sq, sk, sk, sq, sq, sq, sk, sk};
+    for (int t = 0; t < 8; ++t)
+        for (int i = 0; i < 3; ++i) st[3 * t + i] = per[t][i];
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Lq, Lk, D, st, causal, -1,
+                      -1, scale, dtype, stream, true);
+}
+
 int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const float *lse,
               const void *dout, void *dq, void *dk, void *dv, float *delta, int64_t B,
               int64_t H, int64_t Lq, int64_t Lk, int64_t D, const int64_t *strides, int causal,
@@ -395,6 +457,8 @@ const char *fa_status_string(int status)
     case FA_ERR_POINTER: return "a pointer is not device memory of the current device";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_STRIDE: return "a stride is negative or too large, or o has overlapping elements";
+    case FA_ERR_SCRATCH:
+        return "B*H*Lq exceeds the fixed scratch of fa_bwd_noalloc (FA_NOALLOC_MAX_ROWS)";
     default: return "unknown status";
     }
 }

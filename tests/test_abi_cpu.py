@@ -24,6 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_ex", "fa_bwd_kernel_name",
+                                    "fa_bwd_noalloc",
                                     "fa_fwd", "fa_fwd_ex", "fa_kernel_name",
                                     "fa_status_string", "fa_version"]
 
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = fa.fa_status_string(code)
         assert s and s != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -271,3 +272,17 @@ def test_bwd_ex_validation():
     bad = list(st)
     bad[3 * 4 + 2] = 68                        # dout row stride not 16-byte
     assert call(bad) == 6
+
+
+def test_noalloc_rejects_sizes_past_its_scratch_without_touching_a_device():
+    # B*H*Lq beyond the fixed scratch: FA_ERR_SCRATCH before any HIP call
+    p = [(i + 1) << 40 for i in range(9)]
+    Lq = (1 << 21) // 2 + 1
+    rc = fa.fa_bwd_noalloc(*p, 1, 2, Lq, 64, 64, 0, 0.125, 2, None)
+    assert rc == 11 and _lib.STATUS[rc] == "FA_ERR_SCRATCH"
+    # the other checks come first, as in fa_bwd
+    assert fa.fa_bwd_noalloc(*p[:8], None, 1, 2, 64, 64, 64, 0, 0.125, 2, None) == 1
+    assert fa.fa_bwd_noalloc(*p, 1, 2, 64, 64, 96, 0, 0.125, 2, None) == 3
+    assert fa.FA_NOALLOC_MAX_ROWS == 1 << 21
+    text = open(HEADER).read()
+    assert re.search(r"FA_NOALLOC_MAX_ROWS\s+\(1LL << 21\)", text)
