@@ -95,6 +95,12 @@ constexpr float kLazyThreshold = 8.0f;
 // partial row sum over a tile stays at or below this bound (2^15: any single
 // p is then below the fp16 maximum of 65504).
 constexpr float kPpSumBound = 32768.0f;
+// A row that has not seen a key yet (m = -inf) forms its p against this
+// stabiliser instead, -kPpUnseen: every key visible to it then gives
+// p = +inf, its partial sums pass kPpSumBound and the max pass runs, so the
+// first tile needs no test of its own; a tile that hides every key from it
+// gives p = 0 and leaves it unseen.
+constexpr float kPpUnseen = 3.0e38f;
 
 // Normalisation in finite precision.  O's numerator sums the probabilities
 // as rounded for the P.V product, so O is a convex combination of V rows
@@ -589,6 +595,26 @@ __device__ __forceinline__ void dma_16B_sbase(const void *base, uint32_t off, ui
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// A 16-byte LDS load (ds_read_b128) from an LDS byte address.
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+__device__ __forceinline__ u32x4 lds_load_b128(uint32_t a)
+{
+    return *(const lds_u32x4 *)(uintptr_t)a;
+}
+
+// An LDS store the compiler does not see as a memory access.  A tile loop
+// that holds an LDS store the compiler knows of, even on a rare path and
+// even as asm behind a memory clobber, loses the read-ahead schedule of its
+// MFMA phases; a rare path that stages data through LDS stores with this.
+// The compiler orders a later read after it only through data: the store
+// takes the base address `base` of the staged data as an in-out operand,
+// so every address formed from the returned base follows the store (and a
+// wave's LDS operations complete in issue order).
+__device__ __forceinline__ void ds_store_b64_opaque(uint32_t &base, uint32_t off, u32x2 v)
+{
+    __asm__ volatile("ds_write_b64 %1, %2" : "+v"(base) : "v"(base + off), "v"(v));
 }
 
 template <int N>
@@ -1298,7 +1324,8 @@ void fa_fwd_mfma_pp_kernel(Params p)
         // the accumulator share it); in bf16 the largest p is then not a
         // power of two, so O is divided by the sum of the rounded p (see
         // Bf16Ops).  p stays at or below 2^15.  Until a row has seen a key
-        // (m = -inf) the max is always taken (first pass discarded).
+        // (m = -inf) its first pass overflows (kPpUnseen) and the max is
+        // taken.
         auto to_max = [&]() {
             float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -1323,7 +1350,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
         // over the first pass
         float rr;
         auto probs = [&](bool loads) {
-            const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+            const float mc = (m_run == -INFINITY) ? -kPpUnseen : m_run * c;
             float r4[4], r2[2];
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
@@ -1351,9 +1378,8 @@ void fa_fwd_mfma_pp_kernel(Params p)
         };
         // (one rescale site: a second branch around the accumulator made the
         // register allocator copy it on the common path)
-        const bool unseen = WIN ? __any(m_run == -INFINITY) : j == 0;
         float r = probs(true);
-        if (unseen || __any(r > kPpSumBound)) {   // rare: a second pass
+        if (__any(r > kPpSumBound)) {   // rare (and a row's first visible tile)
             to_max();
             r = probs(false);
         }
@@ -1485,6 +1511,545 @@ hipError_t launch_pp(const FwdArgs &a)
     const int64_t nwg = (int64_t)p.BH * p.ntq;
     hipLaunchKernelGGL((fa_fwd_mfma_pp_kernel<Ops, D, CAUSAL, BN, GEN, WIN>), dim3((unsigned)nwg),
                        dim3(512), 0, a.stream, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Persistent ping-pong kernel (pipe 5; contiguous, non-causal, 64-key tiles).
+//
+// The ping-pong kernel (below, pipe 3) pays a fixed cost per workgroup: the
+// first loads and their wait, one idle slot of the second wave group, the
+// discarded first softmax pass and the epilogue, about 15,000 shader cycles
+// in all, or 7% of a workgroup at the mid shape (cycle stamps of every phase
+// of every wave on the part).  Here one workgroup per CU runs the query
+// blocks g, g + G, g + 2G, ... (G = grid size, a multiple of 8, so that every
+// block runs on the XCD that decompose() gives it) as one stream of key
+// tiles: the slots of the ping-pong schedule run on from the last tile of one
+// block into the first tile of the next, so loads, QK^T and softmax of the
+// next block overlap the end of the previous one.  Per block boundary:
+//   * the next block's Q rows are loaded into an LDS stage (64 KB) while the
+//     block's second tile is processed, and copied into the Q^T registers in
+//     the softmax slot of its last tile, right before the MFMA phase that
+//     computes S of the next block's first tile;
+//   * the softmax slot of a block's first tile first stores the previous
+//     block's O and LSE and resets the row state (the accumulator holds the
+//     previous block's last P.V, issued in the slot before).
+// Every tile, block and slot otherwise follows the ping-pong kernel.
+// ---------------------------------------------------------------------------
+template <typename Ops, int D, int BN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_mfma_pers_kernel(Params p)
+{
+    constexpr int NW = 8;
+    constexpr int BM = NW * 32;          // query rows per block
+    constexpr int DC = D / 16;           // 16-dim chunks (k of the QK^T MFMA)
+    constexpr int DB = D / 32;           // 32-dim blocks (rows of O^T)
+    constexpr int KB = BN / 32;          // 32-key blocks (rows of S^T)
+    constexpr int KC = BN / 16;          // 16-key chunks (k of the PV MFMA)
+    constexpr int ROWB = D * 2;          // bytes per K, V or Q row in LDS
+    constexpr int KCH = D / 8;           // 16-byte chunks per row
+    constexpr int TILEB = BN * ROWB;     // bytes of one K (or V) tile
+    constexpr int QB_BYTES = BM * ROWB;  // bytes of the Q stage
+    constexpr int LOADS = TILEB / (NW * 64 * 16);      // loads per wave per tile
+    constexpr int QL = QB_BYTES / (NW * 64 * 16);      // loads per wave per Q stage
+    static_assert(LOADS >= 1 && TILEB % (NW * 64 * 16) == 0, "tile split");
+    static_assert(6 * TILEB + QB_BYTES <= 160 * 1024, "K, V buffers and the Q stage fit the LDS");
+
+    // one LDS array carved by hand: K and V buffers at the bottom, as in the
+    // ping-pong kernel, so their reads keep constant offsets that fit the
+    // 16-bit offset field; the Q stage on top
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[6 * TILEB + QB_BYTES];
+    uint8_t(*k_lds)[TILEB] = reinterpret_cast<uint8_t(*)[TILEB]>(lds);
+    uint8_t(*v_lds)[TILEB] = reinterpret_cast<uint8_t(*)[TILEB]>(lds + 3 * TILEB);
+    uint8_t *q_lds = lds + 6 * TILEB;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;           // waves w and w+4 share a SIMD
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    // ---- the blocks of this workgroup and the tile stream
+    const int nwg = p.BH * p.ntq;
+    const int G = gridDim.x, g = blockIdx.x;
+    const int nitems = (nwg - g + G - 1) / G;    // >= 1: G <= nwg
+    const int n = (p.Lk + BN - 1) / BN;          // tiles per block (>= 4, host-checked)
+    const int T = nitems * n;                    // tiles in the stream
+    auto item = [&](int r, int &bh, int &q_first) {
+        int qt;
+        decompose(g + r * G, nwg, p.BH, p.ntq, false, bh, qt);
+        q_first = qt * BM;
+    };
+    // current block r (of the tile being processed), the next one, and the
+    // one whose output is still to be stored
+    int bh_cur, qf_cur, bh_nxt = 0, qf_nxt = 0, bh_prev = 0, qf_prev = 0;
+    item(0, bh_cur, qf_cur);
+    if (nitems > 1) item(1, bh_nxt, qf_nxt);
+
+    const int64_t seqk = (int64_t)p.Lk * D;      // elements per (b, h) of K and V
+    const int64_t seqq = (int64_t)p.Lq * D;      // elements per (b, h) of Q and O
+
+    // ---- Q^T operand of the first block in VGPRs (rows past Lq read the
+    // last row and are never stored)
+    u32x4 qreg[DC];
+    {
+        const int row = min(qf_cur + wave * 32 + l32, p.Lq - 1);
+        const uint16_t *qh = p.q + (int64_t)bh_cur * seqq;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+            qreg[dc] = *reinterpret_cast<const u32x4 *>(qh + (int64_t)((uint32_t)row * D) +
+                                                        dc * 16 + hi * 8);
+    }
+
+    // ---- loads (as the ping-pong kernel): per-lane source offsets of this
+    // wave's pieces; softmax phases load one tensor, MFMA phases the other
+    int ld_row[LOADS];
+    uint32_t ld_sm[LOADS], ld_mf[LOADS];
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+        const int sl = (r * NW + wave) * 64 + lane;
+        const int row = sl / KCH, pc = sl % KCH;
+        ld_row[r] = row;
+        const uint32_t ov = (uint32_t)(row * D + (pc ^ swz_v<D>(row)) * 8) * 2;
+        const uint32_t ok = (uint32_t)(row * D + (pc ^ swz_k<D>(row)) * 8) * 2;
+        ld_sm[r] = grp == 0 ? ok : ov;
+        ld_mf[r] = grp == 0 ? ov : ok;
+    }
+    const uint32_t k_base = lds_addr(k_lds[0]), v_base = lds_addr(v_lds[0]);
+    struct LoadPlan {
+        const uint16_t *src;
+        uint32_t dst;
+        uint32_t off[LOADS];
+    };
+    // the block of the tile being processed (r, local tile lt) and the
+    // element offsets of the current and the next block within K and V
+    int r = 0, lt = 0;
+    int64_t base_cur = (int64_t)bh_cur * seqk, base_nxt = (int64_t)bh_nxt * seqk;
+    // Element offset of the tile at local index la of the current block's
+    // stream (la >= n: tile la - n of the next block; past the end of the
+    // stream the last tile is fetched again, into a buffer no wave reads any
+    // more) and the last valid key row in it (BN - 1 or more: a whole tile).
+    auto locate = [&](int la, int64_t &off, int &last) {
+        int64_t base = base_cur;
+        int lk = la;
+        if (la >= n) {
+            if (r + 1 < nitems) {
+                base = base_nxt;
+                lk = la - n;
+            } else {
+                lk = n - 1;
+            }
+        }
+        off = base + (int64_t)(lk * BN) * D;
+        last = p.Lk - 1 - lk * BN;
+    };
+    // the loads of one phase into the buffer at byte offset buf_off (rows
+    // past the last valid key fetch that row, as in the ping-pong kernel)
+    auto make_plan = [&](bool is_k, int64_t off, int last, uint32_t buf_off,
+                         const uint32_t (&whole)[LOADS]) {
+        LoadPlan pl;
+        pl.src = (is_k ? p.k : p.v) + off;
+        pl.dst = (is_k ? k_base : v_base) + buf_off + (uint32_t)(wave * 1024);
+#pragma unroll
+        for (int q = 0; q < LOADS; ++q) pl.off[q] = whole[q];
+        if (last < BN - 1) {
+#pragma unroll
+            for (int q = 0; q < LOADS; ++q)
+                pl.off[q] -= (uint32_t)max(ld_row[q] - last, 0) * (uint32_t)(D * 2);
+        }
+        return pl;
+    };
+    auto issue = [&](const LoadPlan &pl, int r) {
+        dma_16B_sbase(pl.src, pl.off[r], pl.dst + (uint32_t)(r * NW * 1024));
+    };
+    // The next block's Q rows into the LDS stage: row i of the block at
+    // byte i * ROWB, 16-byte chunks XOR-swizzled by row as in the K tiles.
+    // (The rare paths below take the lane index through an opaque copy, so
+    // that their addresses are formed when they run rather than hoisted out
+    // of the tile loop into registers held across it.)
+    auto opaque_lane = [&]() {
+        int x = lane;
+        __asm__ volatile("" : "+v"(x));
+        return x;
+    };
+    auto stage_q = [&]() {
+        const uint16_t *qh = p.q + (int64_t)bh_nxt * seqq;
+        const uint32_t dst = lds_addr(q_lds) + (uint32_t)(wave * 1024);
+        const int ln_ = opaque_lane();
+#pragma unroll
+        for (int r = 0; r < QL; ++r) {
+            const int sl = (r * NW + wave) * 64 + ln_;
+            const int row = sl / KCH, pc = sl % KCH;
+            const int src_row = min(qf_nxt + row, p.Lq - 1);
+            const uint32_t off = (uint32_t)(src_row * D + (pc ^ swz_k<D>(row)) * 8) * 2;
+            dma_16B_sbase(qh, off, dst + (uint32_t)(r * NW * 1024));
+        }
+    };
+    auto load_q_from_stage = [&]() {
+        const int ln_ = opaque_lane();
+        const int row = wave * 32 + (ln_ & 31);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+            qreg[dc] = *reinterpret_cast<const u32x4 *>(
+                q_lds + row * ROWB + (((dc * 2 + (ln_ >> 5)) ^ swz_k<D>(row)) * 16));
+    };
+
+    // ---- per-lane LDS read offsets (loop invariant)
+    uint32_t k_rd[DC];
+    {
+        const int row = swap_bits23(l32);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+            k_rd[dc] = (uint32_t)(row * ROWB + (((dc * 2 + hi) ^ swz_k<D>(row)) * 16));
+    }
+    uint32_t v_rd[DB];
+    {
+        const int gq = lane >> 4, t = lane & 15;
+        const int row = 8 * hi + (t >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + 16 * (gq & 1) + 4 * (t & 3);
+            const int cc = col >> 3, within = (col & 7) * 2;
+            v_rd[db] = (uint32_t)(row * ROWB + ((cc ^ swz_v<D>(row)) * 16) + within);
+            __asm__ volatile("" : "+v"(v_rd[db]));
+        }
+    }
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float m_run = -INFINITY, l_part = 0.f, l_rnd = 0.f;
+    const float c = p.c;
+    const float head = pp_headroom<Ops>() / c;
+
+    f32x16 st[KB];
+    u32x4 pk[KC];
+
+    auto qk_mma = [&](const uint8_t *kbuf, int dc, int kb) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(kbuf + k_rd[dc] + kb * 32 * ROWB);
+        if (dc == 0) {
+            f32x16 z;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) z[i] = 0.f;
+            st[kb] = Ops::mma(a, qreg[0], z);
+        } else {
+            st[kb] = Ops::mma(a, qreg[dc], st[kb]);
+        }
+    };
+    constexpr int NPV = KC * DB, NQK = DC * KB;
+    auto read_v = [&](const uint8_t *vbuf, int kc, int db) {
+        const uint8_t *vp = vbuf + v_rd[db] + kc * 16 * ROWB;
+        const uint2 lo = ds_read_tr(vp);
+        const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
+        return u32x4{lo.x, lo.y, hi4.x, hi4.y};
+    };
+    auto load_at = [](int r) { return 2 + r * ((NPV + NQK) / LOADS); };
+    // the MFMA phase of the ping-pong kernel
+    auto mfma_phase = [&](const LoadPlan &pl, const uint8_t *vbuf, const uint8_t *kbuf) {
+        if (PP_PRIO) __builtin_amdgcn_s_setprio(PP_PRIO);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const u32x4 a = read_v(vbuf, kc, db);
+                oacc[db] = Ops::mma(a, pk[kc], oacc[db]);
+#pragma unroll
+                for (int r = 0; r < LOADS; ++r)
+                    if (kc * DB + db == load_at(r)) issue(pl, r);
+            }
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                qk_mma(kbuf, dc, kb);
+#pragma unroll
+                for (int r = 0; r < LOADS; ++r)
+                    if (NPV + dc * KB + kb == load_at(r)) issue(pl, r);
+            }
+        constexpr int LEAD = PP_LEAD;
+        constexpr int NM = NPV + NQK;
+        static_assert(LEAD >= 1 && LEAD <= NPV, "read lead");
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
+#pragma unroll
+        for (int nn = 0; nn < NPV - LEAD; ++nn) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int nn = NPV - LEAD; nn < NM - LEAD; ++nn) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
+        if (PP_PRIO) __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) __asm__ volatile("" : "+v"(st[kb]));
+    };
+    // the softmax phase of the ping-pong kernel for local tile lt
+    auto softmax = [&](const LoadPlan &pl, int lt) {
+        const int k0 = lt * BN;
+        if (k0 + BN > p.Lk) {
+            int top = p.Lk - 1 - k0 - hi * 8;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int cc = kb * 32 + (i >> 3) * 16 + (i & 7);
+                    st[kb][i] = cc <= top ? st[kb][i] : -INFINITY;
+                }
+        }
+        auto to_max = [&]() {
+            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], st[kb][i]);
+            const float mx = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+            const float m_new = fmaxf(m_run, mx + head);
+            const float alpha =
+                (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+            m_run = m_new;
+            l_part *= alpha;
+            if constexpr (Ops::kRoundedNorm) l_rnd *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        };
+        float rr;
+        auto probs = [&](bool loads) {
+            const float mc = (m_run == -INFINITY) ? -kPpUnseen : m_run * c;
+            float r4[4], r2[2];
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                if (loads) {
+#pragma unroll
+                    for (int r = 0; r < LOADS; ++r)
+                        if (kc == r * KC / LOADS) issue(pl, r);
+                }
+                const int kb = kc >> 1, h = kc & 1;
+                float e[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    e[i] = __builtin_amdgcn_exp2f(fmaf(st[kb][h * 8 + i], c, -mc));
+                    r4[i & 3] = kc == 0 && i < 4 ? e[i] : r4[i & 3] + e[i];
+                }
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    pk[kc][w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
+                    if constexpr (Ops::kRoundedNorm)
+                        r2[w & 1] = Ops::add2(pk[kc][w], kc == 0 && w < 2 ? 0.f : r2[w & 1]);
+                }
+            }
+            if constexpr (Ops::kRoundedNorm) rr = r2[0] + r2[1];
+            return (r4[0] + r4[1]) + (r4[2] + r4[3]);
+        };
+        float r = probs(true);
+        if (__any(r > kPpSumBound)) {   // rare (and a block's first tile)
+            to_max();
+            r = probs(false);
+        }
+        l_part += r;
+        if constexpr (Ops::kRoundedNorm) l_rnd += rr;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) __asm__ volatile("" : "+v"(pk[kc]));
+    };
+    // O = acc / l rounded to nearest even and LSE of block (bh, q_first).
+    // The wave's 32 rows pass through its own 8 KB of the Q stage (free at
+    // a block's first tile: the block's Q is in registers, the next block's
+    // is staged one tile later), so that the stores to HBM are whole rows,
+    // 16 bytes per lane and four rows (1 KB of O) per instruction, instead
+    // of 8-byte pieces scattered over 32 rows.
+    auto epilogue = [&](int bh, int q_first) {
+        const float l = half_sum(l_part);
+        const float ln = Ops::kRoundedNorm ? half_sum(l_rnd) : l;
+        const float inv = ln > 0.f ? 1.f / ln : 0.f;
+        const int ln_ = opaque_lane();
+        const int e32 = ln_ & 31, ehi = ln_ >> 5;
+        uint32_t ow = lds_addr(q_lds) + (uint32_t)(wave * (32 * ROWB));
+        {
+            const uint32_t orow = (uint32_t)(e32 * ROWB);
+            const int sw = swz_k<D>(e32);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    // elements db*32 + gg*8 + hi*4 .. +3: 16-byte chunk db*4 + gg
+                    u32x2 x = {Ops::pack2(oacc[db][4 * gg] * inv, oacc[db][4 * gg + 1] * inv),
+                               Ops::pack2(oacc[db][4 * gg + 2] * inv, oacc[db][4 * gg + 3] * inv)};
+                    ds_store_b64_opaque(ow, orow + (uint32_t)(((db * 4 + gg) ^ sw) * 16 + ehi * 8), x);
+                }
+        }
+        const int row0 = q_first + wave * 32;
+        uint16_t *obase = p.o + (int64_t)bh * seqq;
+        constexpr int OPIECES = 32 * KCH / 64;   // 16-byte pieces per lane
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < OPIECES; ++i) {
+            const int idx = i * 64 + ln_, rr = idx / KCH, cc = idx % KCH;
+            const u32x4 val =
+                lds_load_b128(ow + (uint32_t)(rr * ROWB + ((cc ^ swz_k<D>(rr)) * 16)));
+            if (row0 + rr < p.Lq)
+                *reinterpret_cast<u32x4 *>(obase + (int64_t)(row0 + rr) * D + cc * 8) = val;
+            if (i % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        }
+        if (p.lse != nullptr && ehi == 0 && row0 + e32 < p.Lq)
+            p.lse[(int64_t)bh * p.Lq + row0 + e32] =
+                l > 0.f ? m_run * p.scale + __logf(l) : -INFINITY;
+    };
+    const int last_slot = 2 * T + 1;
+    // End of slot t: every load but this slot's has landed (the Q stage and
+    // the stores of an epilogue are issued before the slot's tile loads),
+    // then a barrier; none after group 1's final MFMA phase.
+    auto slot_end = [&](int t) {
+        wait_vmcnt<LOADS>();
+        if (t != last_slot) __syncthreads();
+    };
+
+    // ---- prologue: K_0, V_0, K_1 of the first block
+    {
+        int64_t o0, o1;
+        int l0, l1;
+        locate(0, o0, l0);
+        locate(1, o1, l1);
+        const LoadPlan k0p = make_plan(true, o0, l0, 0, (grp == 0) ? ld_sm : ld_mf);
+        const LoadPlan v0p = make_plan(false, o0, l0, 0, (grp == 0) ? ld_mf : ld_sm);
+        const LoadPlan k1p = make_plan(true, o1, l1, TILEB, (grp == 0) ? ld_sm : ld_mf);
+#pragma unroll
+        for (int q = 0; q < LOADS; ++q) {
+            issue(k0p, q);
+            issue(v0p, q);
+            issue(k1p, q);
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    int t = 0;
+    if (grp == 1) {   // group 1 starts one slot late, loading its share of V_1
+        int64_t o1;
+        int l1;
+        locate(1, o1, l1);
+        const LoadPlan pl = make_plan(false, o1, l1, TILEB, ld_sm);
+#pragma unroll
+        for (int q = 0; q < LOADS; ++q) issue(pl, q);
+        slot_end(t);
+        ++t;
+    }
+    {   // S^T of tile 0 (loads V_1 in group 0's slot 0, K_2 in group 1's slot 1)
+        int64_t o;
+        int l;
+        locate(1 + grp, o, l);
+        const LoadPlan pl = make_plan(grp == 1, o, l, (uint32_t)((1 + grp) * TILEB), ld_mf);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) qk_mma(k_lds[0], dc, kb);
+#pragma unroll
+        for (int q = 0; q < LOADS; ++q) issue(pl, q);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) __asm__ volatile("" : "+v"(st[kb]));
+        slot_end(t);
+        ++t;
+    }
+
+    // Stream tile j (j % 3 == B) of block r at local tile lt.  The loads of
+    // a slot are for stream tiles j + 2 (softmax phase) and j + 2 + grp
+    // (MFMA phase).  Within a block they advance by one tile per tile; the
+    // first two and the last three tiles of a block (where a load or the
+    // rows change block) take one branch that does the block's boundary
+    // work and places the loads afresh.
+    int64_t off_sm = 0, off_mf = 0;   // tiles loaded in the softmax and MFMA phases
+    int last_sm = BN, last_mf = BN;
+    auto tile = [&](auto bc, const uint8_t *vbuf, const uint8_t *kbuf) {
+        constexpr int B = decltype(bc)::value;
+        // softmax phase
+        {
+            if (lt < 2 || lt + 3 >= n) {
+                if (lt == n) {   // the next block
+                    lt = 0;
+                    ++r;
+                    bh_prev = bh_cur;
+                    qf_prev = qf_cur;
+                    bh_cur = bh_nxt;
+                    qf_cur = qf_nxt;
+                    base_cur = base_nxt;
+                    if (r + 1 < nitems) {
+                        item(r + 1, bh_nxt, qf_nxt);
+                        base_nxt = (int64_t)bh_nxt * seqk;
+                    }
+                }
+                if (lt == 1 && r + 1 < nitems) stage_q();
+                locate(lt + 2, off_sm, last_sm);
+                locate(lt + 2 + grp, off_mf, last_mf);
+            } else {
+                off_sm += BN * D;
+                off_mf += BN * D;
+            }
+            // (the two rare steps below sit outside the branch above: inside
+            // it they raise the register count of the whole loop)
+            if (lt == 0 && r > 0) {   // store the previous block, reset the rows
+                epilogue(bh_prev, qf_prev);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+                m_run = -INFINITY;
+                l_part = 0.f;
+                l_rnd = 0.f;
+            }
+            const LoadPlan pl =
+                make_plan(grp == 0, off_sm, last_sm, (uint32_t)(((B + 2) % 3) * TILEB), ld_sm);
+            softmax(pl, lt);
+            // Q of the next block: its first S^T is formed in this tile's
+            // MFMA phase
+            if (lt == n - 1 && r + 1 < nitems) load_q_from_stage();
+            slot_end(t);
+            ++t;
+        }
+        // MFMA phase: P V of this tile, S of the next (of the next block at
+        // the block's last tile)
+        {
+            const uint32_t bo = grp ? (uint32_t)(B * TILEB) : (uint32_t)(((B + 2) % 3) * TILEB);
+            const LoadPlan pl = make_plan(grp == 1, off_mf, last_mf, bo, ld_mf);
+            mfma_phase(pl, vbuf, kbuf);
+            slot_end(t);
+            ++t;
+        }
+        ++lt;
+    };
+    for (int j = 0; j < T; j += 3) {
+        tile(std::integral_constant<int, 0>{}, v_lds[0], k_lds[1]);
+        if (j + 1 >= T) break;
+        tile(std::integral_constant<int, 1>{}, v_lds[1], k_lds[2]);
+        if (j + 2 >= T) break;
+        tile(std::integral_constant<int, 2>{}, v_lds[2], k_lds[0]);
+    }
+    // no load may still be writing LDS when the workgroup ends
+    wait_vmcnt<0>();
+    epilogue(bh_cur, qf_cur);
+}
+
+template <typename Ops, int D, int BN>
+hipError_t launch_pers(const FwdArgs &a, int grid)
+{
+    constexpr int BM = 256;
+    Params p;
+    p.q = static_cast<const uint16_t *>(a.q);
+    p.k = static_cast<const uint16_t *>(a.k);
+    p.v = static_cast<const uint16_t *>(a.v);
+    p.o = static_cast<uint16_t *>(a.o);
+    p.lse = a.lse;
+    p.BH = (int)(a.B * a.H);
+    p.Lq = (int)a.Lq;
+    p.Lk = (int)a.Lk;
+    p.ntq = (int)((a.Lq + BM - 1) / BM);
+    p.scale = a.scale;
+    p.c = a.scale * kLog2e;
+    hipLaunchKernelGGL((fa_fwd_mfma_pers_kernel<Ops, D, BN>), dim3((unsigned)grid), dim3(512), 0,
+                       a.stream, p);
     return hipGetLastError();
 }
 
@@ -1625,9 +2190,34 @@ hipError_t launch_tile_dma(const FwdArgs &a, const MfmaTile &t)
     return hipErrorInvalidConfiguration;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static std::mutex mu;
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0 &&
+        hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus[dev] = 0;
+    return cus[dev];
+}
+
 template <typename Ops>
 hipError_t launch_ops(const FwdArgs &a, const MfmaTile &t)
 {
+    if (t.pipe == 5) {
+        // persistent ping-pong kernel: D = 128, 64-key tiles, non-causal,
+        // at least 4 tiles per block and one block per CU; grid = the CUs
+        // (a multiple of 8), capped at the number of blocks
+        const int64_t nwg = a.B * a.H * ((a.Lq + 255) / 256);
+        const int64_t cus = device_cus();
+        if (!(t.nw == 8 && t.qb == 1 && t.bn == 64 && t.occ == 2) || a.D != 128 || a.causal ||
+            (a.Lk + 63) / 64 < 4 || cus < 8 || nwg < cus)
+            return hipErrorInvalidConfiguration;
+        return launch_pers<Ops, 128, 64>(a, (int)(cus / 8 * 8));
+    }
     if (t.pipe == 3) {
         // 8 waves; 64-key tiles, 96-key tiles at D = 128 (six buffers of 24
         // KB), or 128-key tiles at D = 64 (six buffers of 32 KB would not
@@ -1667,7 +2257,8 @@ bool mfma_supported(const FwdArgs &a)
 MfmaTile mfma_choose_tile(const FwdArgs &a)
 {
     // Static table from an offline sweep of every tile over shape classes
-    // (scaled_dot_product_fa_amd/tune.py, timings in tiles.json).  In short:
+    // (scaled_dot_product_fa_amd/tune.py, timings in tiles.json), after one
+    // rule for the persistent kernel (below).  In short:
     // the ping-pong kernel (8 waves, 256 query rows; 96-key tiles at
     // D = 128, 128-key tiles at D = 64) once there are 512+ blocks of 256
     // rows and 2048+ visible keys per row; at D = 128 non-causal also the
@@ -1684,6 +2275,17 @@ MfmaTile mfma_choose_tile(const FwdArgs &a)
     };
     const int64_t blocks = a.B * a.H * ((a.Lq + 255) / 256);
     const int64_t kv = a.causal ? (a.Lk < a.Lq ? a.Lk : a.Lq) : a.Lk;
+    // Ahead of the table: the persistent ping-pong kernel for short key
+    // sequences (D = 128, non-causal, 4 to 48 key tiles) when every
+    // workgroup gets at least two query blocks.  It saves most of the fixed
+    // cost per query block, which is the larger share the shorter the row:
+    // measured against the 64-key ping-pong kernel at 512 and 1024 blocks,
+    // +21% at 256 keys, +14% at 512, +8% at 1024, +3% at 2048, +1% at 3072,
+    // even at 4096 and -1% to -2% beyond (its tiles cost about 2% more).
+    if (a.D == 128 && !a.causal && a.Lk >= 4 * 64 - 63 && a.Lk <= 48 * 64) {
+        const int64_t g = device_cus() / 8 * 8;
+        if (g >= 8 && blocks >= 2 * g) return MfmaTile{8, 1, 64, 2, 5};
+    }
     for (const TileRule &r : kRules)
         if (r.d == a.D && r.causal == (a.causal ? 1 : 0) && blocks >= r.min_blocks &&
             kv >= r.min_kv)
@@ -1702,11 +2304,12 @@ static const char *intern_name(const char *s)
 }
 
 // "fa_fwd_mfma_<dtype>_d<D>[_causal]_<family><waves>w[<QB>q]_bn<BN>", with
-// family pp (ping-pong), pipe (software-pipelined, LDS DMA) or reg (K/V
-// staged through registers; "_occ<waves per SIMD>" appended).
+// family ppp (persistent ping-pong), pp (ping-pong), pipe (software-
+// pipelined, LDS DMA) or reg (K/V staged through registers; "_occ<waves
+// per SIMD>" appended).
 const char *mfma_kernel_name(const FwdArgs &a, const MfmaTile &t)
 {
-    const char *fam = t.pipe == 3 ? "pp" : t.pipe == 2 ? "pipe" : "reg";
+    const char *fam = t.pipe == 5 ? "ppp" : t.pipe == 3 ? "pp" : t.pipe == 2 ? "pipe" : "reg";
     char buf[96];
     int n = snprintf(buf, sizeof buf, "fa_fwd_mfma_%s_d%d%s_%s%dw", a.dtype == 2 ? "bf16" : "f16",
                      (int)a.D, a.causal ? "_causal" : "", fam, t.nw);
