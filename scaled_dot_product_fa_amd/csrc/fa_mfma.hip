@@ -115,6 +115,7 @@ constexpr float kPpUnseen = 3.0e38f;
 // by the fp32 sum.
 struct Bf16Ops {
     static constexpr bool kRoundedNorm = true;
+    static constexpr bool kSumRounded = false;
     static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -135,8 +136,17 @@ struct Bf16Ops {
     }
 };
 
+// fp16 I/O (ping-pong kernels): the row sum l, for O and for the LSE alike,
+// is the sum of the rounded p (one v_dot2 per pair instead of an fp32 add per
+// score).  It is then exactly the weight P.V used.  fp16 rows keep their
+// stabiliser at the row max, so l >= 1 once a row has seen a key, and each
+// rounded p is within 2^-11 of p (relative) or 2^-25 (absolute, subnormal):
+// the sum moves by at most 2^-11 * l + Lk * 2^-25 <= 2^-10 * l for Lk <=
+// 16384, and the LSE by at most 9.8e-4 in that worst case (every p rounded
+// the same way).
 struct F16Ops {
     static constexpr bool kRoundedNorm = false;
+    static constexpr bool kSumRounded = true;
     static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(
@@ -1364,16 +1374,18 @@ void fa_fwd_mfma_pp_kernel(Params p)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     e[i] = __builtin_amdgcn_exp2f(fmaf(st[kb][h * 8 + i], c, -mc));
-                    r4[i & 3] = kc == 0 && i < 4 ? e[i] : r4[i & 3] + e[i];
+                    if constexpr (!Ops::kSumRounded)
+                        r4[i & 3] = kc == 0 && i < 4 ? e[i] : r4[i & 3] + e[i];
                 }
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     pk[kc][w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
-                    if constexpr (Ops::kRoundedNorm)
+                    if constexpr (Ops::kRoundedNorm || Ops::kSumRounded)
                         r2[w & 1] = Ops::add2(pk[kc][w], kc == 0 && w < 2 ? 0.f : r2[w & 1]);
                 }
             }
             if constexpr (Ops::kRoundedNorm) rr = r2[0] + r2[1];
+            if constexpr (Ops::kSumRounded) return r2[0] + r2[1];
             return (r4[0] + r4[1]) + (r4[2] + r4[3]);
         };
         // (one rescale site: a second branch around the accumulator made the
@@ -1835,16 +1847,18 @@ void fa_fwd_mfma_pers_kernel(Params p)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     e[i] = __builtin_amdgcn_exp2f(fmaf(st[kb][h * 8 + i], c, -mc));
-                    r4[i & 3] = kc == 0 && i < 4 ? e[i] : r4[i & 3] + e[i];
+                    if constexpr (!Ops::kSumRounded)
+                        r4[i & 3] = kc == 0 && i < 4 ? e[i] : r4[i & 3] + e[i];
                 }
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     pk[kc][w] = Ops::pack2(e[2 * w], e[2 * w + 1]);
-                    if constexpr (Ops::kRoundedNorm)
+                    if constexpr (Ops::kRoundedNorm || Ops::kSumRounded)
                         r2[w & 1] = Ops::add2(pk[kc][w], kc == 0 && w < 2 ? 0.f : r2[w & 1]);
                 }
             }
             if constexpr (Ops::kRoundedNorm) rr = r2[0] + r2[1];
+            if constexpr (Ops::kSumRounded) return r2[0] + r2[1];
             return (r4[0] + r4[1]) + (r4[2] + r4[3]);
         };
         float r = probs(true);
