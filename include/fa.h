@@ -79,15 +79,24 @@ enum fa_status {
  *   p_ij = exp(s_ij - m_i) / l_i,  s_ij = scale * q[b,h,i,:] . k[b,h,j,:],
  *   lse[b,h,i] = m_i + log(l_i).
  * bf16/fp16 inputs are multiplied exactly and accumulated in fp32; the
- * softmax runs in fp32; o is rounded to nearest-even into the I/O type.
+ * softmax runs in fp32; p is rounded to nearest-even into the I/O type for
+ * the product with v, and o is divided by the sum of those rounded p (the
+ * weights it was built from), then rounded to nearest-even into the I/O
+ * type.  lse takes l from the fp32 sum of p for bf16, and from the sum of
+ * the rounded p for fp16 (within 2^-10 of the fp32 sum: at most 9.8e-4 on
+ * lse for rows up to 16384 keys).
  *
  * Ownership: the caller owns every buffer; the library allocates nothing,
  * keeps no state between calls and may be called from several threads.
  * o and lse must not overlap q, k, v or each other.
  *
- * Errors: every check runs on the host before anything is enqueued; on an
- * error nothing is written and nothing is launched.  The launch itself is
- * asynchronous: a device fault appears at the caller's next synchronisation.
+ * Errors: every check runs on the host before anything is enqueued, in
+ * this order: NULL pointers, sizes and limits, head dimension, dtype, scale,
+ * alignment and overlaps use no HIP call; the last check, FA_ERR_POINTER,
+ * asks the HIP runtime (hipGetDevice, hipPointerGetAttributes) whether each
+ * pointer is device memory of the current device.  On an error nothing is
+ * written and nothing is launched.  The launch itself is asynchronous: a
+ * device fault appears at the caller's next synchronisation.
  * Returns FA_OK or an enum fa_status code.
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -228,10 +237,17 @@ int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
 const char *fa_status_string(int status);
 
 /*
- * fa_kernel_name -- name of the kernel fa_fwd would launch for these
+ * fa_kernel_name -- label of the kernel fa_fwd would launch for these
  * arguments (a static string), or NULL when fa_fwd would reject the shape,
- * head dimension, dtype or scale.  Pure host logic: touches no device.
- * Used to label measurements and to match profiler output.
+ * head dimension, dtype or scale.  MFMA kernels are labelled
+ * "fa_fwd_mfma_<bf16|f16>_d<D>[_causal]_<family><waves>w[<QB>q]_bn<keys>",
+ * family ppp (persistent ping-pong), pp (ping-pong), pipe (software-
+ * pipelined) or reg (register-staged, "_occ<waves per SIMD>" appended);
+ * the vector-ALU kernel "fa_fwd_valu_<type>_d<D>[_causal]".  Host logic: it
+ * launches and allocates nothing, but the choice of the persistent kernel
+ * depends on the current device's compute-unit count (one HIP attribute
+ * query; with no device that kernel is never named).  Used to label
+ * measurements and to match profiler output.
  */
 const char *fa_kernel_name(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                            int64_t D, int causal, float scale, int dtype);
