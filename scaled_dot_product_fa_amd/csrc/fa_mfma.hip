@@ -1475,24 +1475,42 @@ void fa_fwd_mfma_pp_kernel(Params p)
         wait_vmcnt<0>();
     }
 
-    // ---- epilogue: O = acc / l, rounded to nearest even; LSE = m*scale + ln l
+    // ---- epilogue: O = acc / l, rounded to nearest even; LSE = m*scale + ln l.
+    // Every wave past its last LDS read and load (the barrier), each wave's
+    // 32 rows of O pass through its own 32 rows' worth of the K/V buffers
+    // (waves 0-3 in the K buffers, 4-7 in the V buffers), so that the stores
+    // to HBM are whole rows: 16 bytes per lane and four rows of O per
+    // instruction, instead of 8-byte pieces scattered over 32 rows.  (The
+    // next workgroup on this CU needs the whole LDS allocation, so waiting
+    // here for the later wave group delays nothing.)
     const float l = half_sum(l_part);
     const float ln = Ops::kRoundedNorm ? half_sum(l_rnd) : l;
-    if (qrow < p.Lq) {
-        const float inv = ln > 0.f ? 1.f / ln : 0.f;
-        uint16_t *orow = p.o + og_base + (int64_t)qrow * o_sl;
+    const float inv = ln > 0.f ? 1.f / ln : 0.f;
+    __syncthreads();
+    uint32_t ob = (wave < 4 ? k_base : v_base) + (uint32_t)((wave & 3) * 32 * ROWB);
+    {
+        const uint32_t orow = (uint32_t)(l32 * ROWB);
+        const int sw = swz_k<D>(l32);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int d = db * 32 + g * 8 + hi * 4;
+                // elements db*32 + g*8 + hi*4 .. +3: 16-byte chunk db*4 + g
                 u32x2 x = {Ops::pack2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
                            Ops::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-                *reinterpret_cast<u32x2 *>(orow + d) = x;
+                ds_store_b64_opaque(ob, orow + (uint32_t)(((db * 4 + g) ^ sw) * 16 + hi * 8), x);
             }
-        if (p.lse != nullptr && hi == 0)
-            p.lse[(int64_t)bh * p.Lq + qrow] = l > 0.f ? m_run * p.scale + __logf(l) : -INFINITY;
     }
+    constexpr int OPIECES = 32 * KCH / 64;   // 16-byte pieces per lane
+#pragma unroll
+    for (int i = 0; i < OPIECES; ++i) {
+        const int idx = i * 64 + lane, rr = idx / KCH, cc = idx % KCH;
+        const u32x4 val = lds_load_b128(ob + (uint32_t)(rr * ROWB + ((cc ^ swz_k<D>(rr)) * 16)));
+        if (qw + rr < p.Lq)
+            *reinterpret_cast<u32x4 *>(p.o + og_base + (int64_t)(qw + rr) * o_sl + cc * 8) = val;
+    }
+    if (p.lse != nullptr && hi == 0 && qrow < p.Lq)
+        p.lse[(int64_t)bh * p.Lq + qrow] = l > 0.f ? m_run * p.scale + __logf(l) : -INFINITY;
 }
 
 template <typename Ops, int D, bool CAUSAL, int BN, bool GEN = false, bool WIN = false>
