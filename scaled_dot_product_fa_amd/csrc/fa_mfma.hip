@@ -2308,13 +2308,13 @@ MfmaTile mfma_choose_tile(const FwdArgs &a)
     const int64_t blocks = a.B * a.H * ((a.Lq + 255) / 256);
     const int64_t kv = a.causal ? (a.Lk < a.Lq ? a.Lk : a.Lq) : a.Lk;
     // Ahead of the table: the persistent ping-pong kernel for short key
-    // sequences (D = 128, non-causal, 4 to 48 key tiles) when every
+    // sequences (D = 128, non-causal, 4 to 16 key tiles) when every
     // workgroup gets at least two query blocks.  It saves most of the fixed
     // cost per query block, which is the larger share the shorter the row:
     // measured against the 64-key ping-pong kernel at 512 and 1024 blocks,
-    // +21% at 256 keys, +14% at 512, +8% at 1024, +3% at 2048, +1% at 3072,
-    // even at 4096 and -1% to -2% beyond (its tiles cost about 2% more).
-    if (a.D == 128 && !a.causal && a.Lk >= 4 * 64 - 63 && a.Lk <= 48 * 64) {
+    // +6% to +8% at 256 keys, +3% at 512, +0.5% at 1024, -1% at 2048 and
+    // 3072 (its tiles cost about 2% more).
+    if (a.D == 128 && !a.causal && a.Lk >= 4 * 64 - 63 && a.Lk <= 16 * 64) {
         const int64_t g = device_cus() / 8 * 8;
         if (g >= 8 && blocks >= 2 * g) return MfmaTile{8, 1, 64, 2, 5};
     }
