@@ -275,18 +275,51 @@ __device__ __forceinline__ u32x4 read_tr(const uint8_t *tile, const uint32_t (&o
     return u32x4{lo.x, lo.y, hi4.x, hi4.y};
 }
 
-// Store a 32(dims) x 32(columns) accumulator block: the lane owns column
-// l32 and dims 32*db + 8*g + 4*hi + (0..3) for g = 0..3.
-template <typename Ops>
-__device__ __forceinline__ void store_cols(uint16_t *row_base, int db, int hi, const f32x16 &acc,
-                                           float mul)
+// An 8-byte LDS store the compiler does not see as one: an LDS store it
+// knows of anywhere in a kernel makes it drop the read-ahead schedule of the
+// MFMA steps.  `base` is an in-out operand, so every address formed from it
+// afterwards follows the store (and a wave's LDS operations complete in
+// issue order).
+__device__ __forceinline__ void ds_store_b64_opaque(uint32_t &base, uint32_t off, uint2 v)
 {
+    __asm__ volatile("ds_write_b64 %1, %2" : "+v"(base) : "v"(base + off), "v"(v));
+}
+
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+__device__ __forceinline__ u32x4 lds_load_b128(uint32_t a)
+{
+    return *(const lds_u32x4 *)(uintptr_t)a;
+}
+
+// A wave's 32 rows of gradient (the accumulator layout: lane l32 + 32*hi
+// holds row l32, columns db*32 + 8g + 4hi .. +3 in acc[db][4g .. 4g+3]),
+// times `mul`, rounded to the I/O type and stored as whole rows: through 32
+// rows of this wave's own LDS at `stage` (16-byte chunk c of row r at
+// position c ^ (r mod D/8)), then 16-byte pieces, four rows (D = 128) per
+// store instruction instead of 8-byte pieces over 32 rows.  Rows >= nrows
+// are not stored.
+template <typename Ops, int D>
+__device__ __forceinline__ void store_rows_staged(uint32_t stage, const f32x16 (&acc)[D / 32],
+                                                  float mul, uint16_t *row0, int64_t row_stride,
+                                                  int nrows, int lane)
+{
+    constexpr int ROWB = D * 2, CH = D / 8, DB = D / 32;
+    const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        uint2 w;
-        w.x = Ops::pack2(acc[4 * g] * mul, acc[4 * g + 1] * mul);
-        w.y = Ops::pack2(acc[4 * g + 2] * mul, acc[4 * g + 3] * mul);
-        *(uint2 *)(row_base + db * 32 + 8 * g + 4 * hi) = w;
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            uint2 w;
+            w.x = Ops::pack2(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul);
+            w.y = Ops::pack2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
+            ds_store_b64_opaque(
+                stage, (uint32_t)(l32 * ROWB + (((db * 4 + g) ^ (l32 % CH)) * 16) + hi * 8), w);
+        }
+#pragma unroll
+    for (int i = 0; i < 32 * CH / 64; ++i) {
+        const int idx = i * 64 + lane, rr = idx / CH, cc = idx % CH;
+        const u32x4 val = lds_load_b128(stage + (uint32_t)(rr * ROWB + ((cc ^ (rr % CH)) * 16)));
+        if (rr < nrows) *(u32x4 *)(row0 + (int64_t)rr * row_stride + cc * 8) = val;
     }
 }
 
@@ -318,6 +351,7 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
     constexpr int NBUF = 4;
     static_assert(NLD >= 1 && BQ * CH % kThreads == 0, "tile split");
     __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * BUFB];
+    static_assert(NW * 2 * 32 * ROWB <= NBUF * BUFB, "dK, dV staging fits the LDS");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -537,14 +571,16 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
     }
     wait_vmcnt<0>();
 
-    if (key < Lk) {
-        uint16_t *dkr = p.dk + dk_b + (int64_t)key * dk_sl;
-        uint16_t *dvr = p.dv + dv_b + (int64_t)key * dv_sl;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            store_cols<Ops>(dkr, db, hi, dk[db], p.scale);
-            store_cols<Ops>(dvr, db, hi, dv[db], 1.f);
-        }
+    // dK and dV as whole rows through the LDS, free once every wave is past
+    // its last step: each wave uses its own 2 x 32 rows
+    __syncthreads();
+    {
+        const uint32_t st = smem_base + (uint32_t)(wave * 2 * 32 * ROWB);
+        const int nk = min(32, Lk - kw);
+        store_rows_staged<Ops, D>(st, dk, p.scale, p.dk + dk_b + (int64_t)kw * dk_sl, dk_sl, nk,
+                                  lane);
+        store_rows_staged<Ops, D>(st + (uint32_t)(32 * ROWB), dv, 1.f,
+                                  p.dv + dv_b + (int64_t)kw * dv_sl, dv_sl, nk, lane);
     }
 }
 
@@ -566,6 +602,7 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
     constexpr int BUFB = 2 * TILEB;
     static_assert(NLD >= 1 && BN * CH % (NW * 64) == 0, "tile split");
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUFB];
+    static_assert(NW * 32 * ROWB <= 2 * BUFB, "dQ staging fits the LDS");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -723,11 +760,10 @@ void fa_bwd_dq_mfma_kernel(BwdParams p)
         __syncthreads();
     }
 
-    if (row_ok) {
-        uint16_t *dqr = p.dq + dq_b + (int64_t)qrow * dq_sl;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) store_cols<Ops>(dqr, db, hi, dq[db], p.scale);
-    }
+    // dQ as whole rows through the LDS (every tile ends with a barrier, so
+    // no wave reads it any more): 32 rows per wave
+    store_rows_staged<Ops, D>(smem_base + (uint32_t)(wave * 32 * ROWB), dq, p.scale,
+                              p.dq + dq_b + (int64_t)qw * dq_sl, dq_sl, min(32, Lq - qw), lane);
 }
 
 template <typename Ops, int D, bool CAUSAL, bool GEN, bool WIN>
