@@ -2290,15 +2290,15 @@ MfmaTile mfma_choose_tile(const FwdArgs &a)
 {
     // Static table from an offline sweep of every tile over shape classes
     // (scaled_dot_product_fa_amd/tune.py, timings in tiles.json), after one
-    // rule for the persistent kernel (below).  In short:
-    // the ping-pong kernel (8 waves, 256 query rows; 96-key tiles at
-    // D = 128, 128-key tiles at D = 64) once there are 512+ blocks of 256
-    // rows and 2048+ visible keys per row; at D = 128 non-causal also the
-    // 64-key ping-pong kernel from 128 blocks; otherwise 4 waves of the
-    // software-pipelined kernel (128 rows per workgroup, twice as many
-    // workgroups).
+    // rule for the persistent kernel (below).  Rules are per I/O type; the
+    // bf16 and fp16 sweeps pick the same tiles.  In short: the ping-pong
+    // kernel (8 waves, 256 query rows) once there are 512+ blocks of 256
+    // rows and 2048+ visible keys per row (64-key tiles at D = 128
+    // non-causal, 96-key causal, 128-key at D = 64); non-causal also from
+    // 128 blocks (64-key tiles); otherwise 4 waves of the software-pipelined
+    // kernel (128 rows per workgroup, twice as many workgroups).
     struct TileRule {
-        int d, causal;
+        int dtype, d, causal;
         int64_t min_blocks, min_kv;
         MfmaTile tile;
     };
@@ -2319,8 +2319,8 @@ MfmaTile mfma_choose_tile(const FwdArgs &a)
         if (g >= 8 && blocks >= 2 * g) return MfmaTile{8, 1, 64, 2, 5};
     }
     for (const TileRule &r : kRules)
-        if (r.d == a.D && r.causal == (a.causal ? 1 : 0) && blocks >= r.min_blocks &&
-            kv >= r.min_kv)
+        if (r.dtype == a.dtype && r.d == a.D && r.causal == (a.causal ? 1 : 0) &&
+            blocks >= r.min_blocks && kv >= r.min_kv)
             return r.tile;
     return MfmaTile{4, 1, 64, 2, 2};
 }
