@@ -580,6 +580,13 @@ __device__ __forceinline__ uint2 ds_read_tr(const uint8_t *p)
     return __builtin_bit_cast(uint2, r);
 }
 
+// The same read at an LDS byte address.
+__device__ __forceinline__ uint2 ds_read_tr_at(uint32_t a)
+{
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)a);
+    return __builtin_bit_cast(uint2, r);
+}
+
 // One global_load_lds_dwordx4: the wave's 64 lanes each fetch 16 bytes from
 // their own global address and the hardware writes them to LDS at m0 +
 // 16 * lane.  Issued from inline assembly on purpose: the compiler treats
@@ -1733,6 +1740,11 @@ void fa_fwd_mfma_pers_kernel(Params p)
         for (int dc = 0; dc < DC; ++dc)
             k_rd[dc] = (uint32_t)(row * ROWB + (((dc * 2 + hi) ^ swz_k<D>(row)) * 16));
     }
+    // V read addresses in LDS, absolute (base of V buffer 0 included): the
+    // V buffers end above 64 KB, and with the base folded into the register
+    // every read of every buffer keeps an immediate offset below 64 KB
+    // (buffer * TILEB + key chunk), where a buffer-relative register would
+    // need an add before each read of buffers 1 and 2
     uint32_t v_rd[DB];
     {
         const int gq = lane >> 4, t = lane & 15;
@@ -1741,7 +1753,7 @@ void fa_fwd_mfma_pers_kernel(Params p)
         for (int db = 0; db < DB; ++db) {
             const int col = db * 32 + 16 * (gq & 1) + 4 * (t & 3);
             const int cc = col >> 3, within = (col & 7) * 2;
-            v_rd[db] = (uint32_t)(row * ROWB + ((cc ^ swz_v<D>(row)) * 16) + within);
+            v_rd[db] = v_base + (uint32_t)(row * ROWB + ((cc ^ swz_v<D>(row)) * 16) + within);
             __asm__ volatile("" : "+v"(v_rd[db]));
         }
     }
@@ -1770,21 +1782,21 @@ void fa_fwd_mfma_pers_kernel(Params p)
         }
     };
     constexpr int NPV = KC * DB, NQK = DC * KB;
-    auto read_v = [&](const uint8_t *vbuf, int kc, int db) {
-        const uint8_t *vp = vbuf + v_rd[db] + kc * 16 * ROWB;
-        const uint2 lo = ds_read_tr(vp);
-        const uint2 hi4 = ds_read_tr(vp + 4 * ROWB);
+    auto read_v = [&](int vb, int kc, int db) {
+        const uint32_t a = v_rd[db] + (uint32_t)(vb * TILEB + kc * 16 * ROWB);
+        const uint2 lo = ds_read_tr_at(a);
+        const uint2 hi4 = ds_read_tr_at(a + 4 * ROWB);
         return u32x4{lo.x, lo.y, hi4.x, hi4.y};
     };
     auto load_at = [](int r) { return 2 + r * ((NPV + NQK) / LOADS); };
     // the MFMA phase of the ping-pong kernel
-    auto mfma_phase = [&](const LoadPlan &pl, const uint8_t *vbuf, const uint8_t *kbuf) {
+    auto mfma_phase = [&](const LoadPlan &pl, int vb, const uint8_t *kbuf) {
         if (PP_PRIO) __builtin_amdgcn_s_setprio(PP_PRIO);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const u32x4 a = read_v(vbuf, kc, db);
+                const u32x4 a = read_v(vb, kc, db);
                 oacc[db] = Ops::mma(a, pk[kc], oacc[db]);
 #pragma unroll
                 for (int r = 0; r < LOADS; ++r)
@@ -1995,7 +2007,7 @@ void fa_fwd_mfma_pers_kernel(Params p)
     // work and places the loads afresh.
     int64_t off_sm = 0, off_mf = 0;   // tiles loaded in the softmax and MFMA phases
     int last_sm = BN, last_mf = BN;
-    auto tile = [&](auto bc, const uint8_t *vbuf, const uint8_t *kbuf) {
+    auto tile = [&](auto bc, const uint8_t *kbuf) {
         constexpr int B = decltype(bc)::value;
         // softmax phase
         {
@@ -2046,18 +2058,18 @@ void fa_fwd_mfma_pers_kernel(Params p)
         {
             const uint32_t bo = grp ? (uint32_t)(B * TILEB) : (uint32_t)(((B + 2) % 3) * TILEB);
             const LoadPlan pl = make_plan(grp == 1, off_mf, last_mf, bo, ld_mf);
-            mfma_phase(pl, vbuf, kbuf);
+            mfma_phase(pl, B, kbuf);
             slot_end(t);
             ++t;
         }
         ++lt;
     };
     for (int j = 0; j < T; j += 3) {
-        tile(std::integral_constant<int, 0>{}, v_lds[0], k_lds[1]);
+        tile(std::integral_constant<int, 0>{}, k_lds[1]);
         if (j + 1 >= T) break;
-        tile(std::integral_constant<int, 1>{}, v_lds[1], k_lds[2]);
+        tile(std::integral_constant<int, 1>{}, k_lds[2]);
         if (j + 2 >= T) break;
-        tile(std::integral_constant<int, 2>{}, v_lds[2], k_lds[0]);
+        tile(std::integral_constant<int, 2>{}, k_lds[0]);
     }
     // no load may still be writing LDS when the workgroup ends
     wait_vmcnt<0>();
@@ -2308,13 +2320,13 @@ MfmaTile mfma_choose_tile(const FwdArgs &a)
     const int64_t blocks = a.B * a.H * ((a.Lq + 255) / 256);
     const int64_t kv = a.causal ? (a.Lk < a.Lq ? a.Lk : a.Lq) : a.Lk;
     // Ahead of the table: the persistent ping-pong kernel for short key
-    // sequences (D = 128, non-causal, 4 to 16 key tiles) when every
+    // sequences (D = 128, non-causal, 4 to 32 key tiles) when every
     // workgroup gets at least two query blocks.  It saves most of the fixed
     // cost per query block, which is the larger share the shorter the row:
     // measured against the 64-key ping-pong kernel at 512 and 1024 blocks,
-    // +6% to +8% at 256 keys, +3% at 512, +0.5% at 1024, -1% at 2048 and
-    // 3072 (its tiles cost about 2% more).
-    if (a.D == 128 && !a.causal && a.Lk >= 4 * 64 - 63 && a.Lk <= 16 * 64) {
+    // +7% to +9% at 256 keys, +4% at 512, +2% to +3% at 1024, +1% at 2048,
+    // even at 3072 (its tiles cost about 0.8% more).
+    if (a.D == 128 && !a.causal && a.Lk >= 4 * 64 - 63 && a.Lk <= 32 * 64) {
         const int64_t g = device_cus() / 8 * 8;
         if (g >= 8 && blocks >= 2 * g) return MfmaTile{8, 1, 64, 2, 5};
     }

@@ -84,14 +84,15 @@ def test_persistent_stabiliser_moves(monkeypatch):
 
 
 def test_persistent_is_the_default_for_short_rows():
-    """D=128 non-causal rows of 193..1024 keys with two or more blocks per
+    """D=128 non-causal rows of 193..2048 keys with two or more blocks per
     workgroup take the persistent kernel; longer rows, causal calls and a
     single block per workgroup keep the ping-pong kernel."""
     n = cus()
     H = 2 * n // 4          # B=1, Lq=1024: 4 blocks per head -> 2 blocks per CU
     assert "ppp8w" in fa.fa_kernel_name(1, H, 1024, 1024, 128, 0, 0.088, 2)
     assert "ppp8w" in fa.fa_kernel_name(1, H, 1024, 193, 128, 0, 0.088, 1)
-    assert "ppp8w" not in fa.fa_kernel_name(1, H, 1024, 1025, 128, 0, 0.088, 2)
+    assert "ppp8w" in fa.fa_kernel_name(1, H, 1024, 2048, 128, 0, 0.088, 2)
+    assert "ppp8w" not in fa.fa_kernel_name(1, H, 1024, 2049, 128, 0, 0.088, 2)
     assert "ppp8w" not in fa.fa_kernel_name(1, H, 1024, 4096, 128, 0, 0.088, 2)
     assert "ppp8w" not in fa.fa_kernel_name(1, H, 1024, 1024, 128, 1, 0.088, 2)
     assert "ppp8w" not in fa.fa_kernel_name(1, H, 1024, 192, 128, 0, 0.088, 2)
