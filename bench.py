@@ -19,8 +19,11 @@ Per shape the run is:
   4. `sustained`: --trials (default 5) further timed runs of at least
      --trial-ms (default 200) ms each, HIP events around each; median and
      minimum per-launch time.
-The graphics clock is sampled in-process (amdsmi, no child process) during
-steps 3 and 4 and reported with the peak that clock allows.
+The graphics clock is sampled in-process (amdsmi, no child process) and
+reported for steps 3 and 4 with the peak that clock allows.  The sampler
+(amdsmi's initialisation and its thread) starts before step 1: started
+just before step 3, the launches of the next few tens of milliseconds ran
+up to 20% slower, enough to move the line of a 140 us kernel by 4-6%.
 
 The metric names two shapes, D=128 N=4096 and N=16384, non-causal: the line's
 `value` is the first (the mid workload), and `secondary` carries the same
@@ -106,6 +109,7 @@ class ClockSampler:
         self.source = None
         self._stop = None
         self._thread = None
+        self.recording = False   # samples are kept only while True
         try:
             import amdsmi
             import torch
@@ -133,7 +137,9 @@ class ClockSampler:
         def loop():
             while not self._stop.is_set():
                 try:
-                    self.samples.append(self.read())
+                    x = self.read()
+                    if self.recording:
+                        self.samples.append(x)
                 except Exception:  # noqa: BLE001
                     pass
                 self._stop.wait(self.period)
@@ -160,7 +166,13 @@ class ClockSampler:
 def measure(launch, stream, steps, warmup, settle_s, trials, trial_ms):
     """Settle, warm up, time exactly `steps` launches, then `trials`
     sustained runs of at least `trial_ms` ms each.  Returns timings (ms per
-    launch) and the clock summary."""
+    launch) and the clock summary of the timed launches."""
+    clock = ClockSampler()
+    with clock:
+        return _measure(launch, stream, steps, warmup, settle_s, trials, trial_ms, clock)
+
+
+def _measure(launch, stream, steps, warmup, settle_s, trials, trial_ms, clock):
     import torch
     dev = torch.device("cuda:0")
     n_settle = 0
@@ -173,29 +185,29 @@ def measure(launch, stream, steps, warmup, settle_s, trials, trial_ms):
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize(dev)
-    clock = ClockSampler()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    with clock:
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        for _ in range(steps):
+    clock.recording = True
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        launch()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    kernel_ms = ev0.elapsed_time(ev1) / steps
+    per_trial = max(steps, int(math.ceil(trial_ms / max(kernel_ms, 1e-3))))
+    trial_ms_list = []
+    for _ in range(trials):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(per_trial):
             launch()
-        ev1.record(stream)
+        b.record(stream)
         torch.cuda.synchronize(dev)
-        t1 = time.perf_counter()
-        kernel_ms = ev0.elapsed_time(ev1) / steps
-        per_trial = max(steps, int(math.ceil(trial_ms / max(kernel_ms, 1e-3))))
-        trial_ms_list = []
-        for _ in range(trials):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(per_trial):
-                launch()
-            b.record(stream)
-            torch.cuda.synchronize(dev)
-            trial_ms_list.append(a.elapsed_time(b) / per_trial)
+        trial_ms_list.append(a.elapsed_time(b) / per_trial)
+    clock.recording = False
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     srt = sorted(trial_ms_list)
     return dict(wall_ms=(t1 - t0) * 1e3 / steps, kernel_ms=kernel_ms,
