@@ -38,6 +38,10 @@ the mid workload fits its ~15 s budget; larger workloads use a seeded row
 sample) and ``parity`` (every row the CPU baseline computed, compared with
 this run's GPU output).
 
+With --curve the run only times the forward over sequence lengths 512 to
+16384 at a fixed 16384 tokens and model width 2048 (D = 64 and 128, both
+masks) and prints one JSON line with every point.
+
 With --backward one step is one fa_bwd call (the delta, dK/dV and dQ kernels
 in order on one stream) over the same inputs plus a seeded dO, with o and lse
 from one forward call made before timing.  FLOPs per step are the
@@ -492,6 +496,53 @@ def forward_entry(w, causal, r, layout="bhld", window=None):
     }
 
 
+CURVE_N = (512, 1024, 2048, 4096, 8192, 16384)
+
+
+def seqlen_curve(settle_s=0.5, steps=40, warmup=10):
+    """Forward TFLOP/s against sequence length at a fixed token count: for
+    N = 512 ... 16384, B = 16384 / N sequences of N tokens, model width 2048
+    (H = 2048 / D heads), D = 64 and 128, non-causal and causal, bf16, iid
+    N(0, 1) inputs.  Per point: settling launches, a warm-up, then `steps`
+    launches between HIP events.  One JSON line with every point."""
+    import torch
+    import scaled_dot_product_fa_amd as fa
+    from scaled_dot_product_fa_amd import inputs
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    points = []
+    for D in (128, 64):
+        H = 2048 // D
+        for causal in (False, True):
+            for N in CURVE_N:
+                B = 16384 // N
+                w = inputs.Workload(f"curve{N}", B, H, N, N, D, "bf16",
+                                    1.0 / math.sqrt(D), 11, ("noncausal", "causal"))
+                q, k, v = (t.to(dev) for t in inputs.workload_inputs(w))
+                o = torch.empty_like(q)
+                lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+                name = fa.fa_kernel_name(B, H, N, N, D, int(causal), w.scale,
+                                         fa.dtype_code(q.dtype))
+
+                def launch():
+                    fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse,
+                               stream=stream)
+                r = measure(launch, stream, steps, warmup, settle_s, 0, 0.0)
+                tf = w.flops(causal) / (r["kernel_ms"] * 1e-3) / 1e12
+                pt = {"D": D, "causal": causal, "N": N, "B": B, "H": H, "kernel": name,
+                      "kernel_ms": round(r["kernel_ms"], 5), "tflops": round(tf, 1),
+                      "frac": round(tf / 2500.0, 4), "mhz_mean": r["clock"].get("mhz_mean")}
+                points.append(pt)
+                log(f"curve: D={D} {'causal' if causal else 'non-causal'} N={N} B={B} "
+                    f"H={H} {name}: {r['kernel_ms'] * 1e3:.1f} us, {tf:.1f} TFLOP/s, "
+                    f"clock {pt['mhz_mean']} MHz")
+                del q, k, v, o, lse
+    print(json.dumps({"metric": "attention fwd TFLOP/s vs sequence length "
+                      "(16384 tokens, width 2048, bf16)", "unit": "TFLOP/s",
+                      "n_gpus": 1, "steps": steps, "warmup": warmup, "settle_s": settle_s,
+                      "data": "synthetic", "points": points}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -519,6 +570,10 @@ def main():
                     help="skip the 16K non-causal forward (the metric's second "
                          "shape), which runs by default after the mid workload")
     ap.add_argument("--secondary", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--curve", action="store_true",
+                    help="only time the forward over sequence lengths 512..16384 "
+                         "at 16384 tokens and width 2048 (D=64 and 128, both "
+                         "masks), then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for scaling "
                          "HBM byte counters), then exit")
@@ -534,6 +589,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.curve:
+        seqlen_curve()
+        return
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
