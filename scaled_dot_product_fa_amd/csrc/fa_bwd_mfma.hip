@@ -22,7 +22,11 @@
 //     holds one key column and two runs of 8 consecutive queries.  P and dS,
 //     rounded to the I/O type, are then directly the B operands of
 //     dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T come from the same LDS
-//     tiles through ds_read_b64_tr_b16 (transposing reads).
+//     tiles through ds_read_b64_tr_b16 (transposing reads).  At D = 128 (one
+//     wave per SIMD, nothing else to fill the MFMA pipe's idle time) a step
+//     forms S/dP of the next tile while the vector ALU turns the previous
+//     step's S/dP into P and dS, then runs dV/dK; at D = 64 (two waves per
+//     SIMD) the probabilities follow their own S/dP within a step.
 //   * dQ kernel, one workgroup per block of query rows, the forward's layout:
 //     each wave owns 32 queries with Q^T and dO^T in VGPRs; tiles of 64 keys
 //     of K and V stream through LDS (direct loads, two buffers); S^T = K Q^T
@@ -46,8 +50,9 @@
 //
 // Compile-time knobs (defaults are the measured best): waves per SIMD each
 // kernel is register-budgeted for, at D = 64 and D = 128 (BWD_*_OCC*), and
-// whether the dK/dV step pins its MFMA / LDS-read / VALU interleave with
-// sched_group_barrier (BWD_KV_SCHED; BWD_KV_VPER VALU ops per slot).
+// whether the dK/dV step pins its MFMA / LDS-read / VALU interleave
+// (BWD_KV_SCHED: sched_group_barrier with BWD_KV_VPER VALU ops per slot at
+// two waves per SIMD, sched_barrier fences between the chunks at one).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -461,19 +466,25 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
             dp = Ops::mma(ag[dc], vop[dc], dp);
         }
     };
-    // Probabilities and ds of the tile at rows i0.. (in LDS at b).  TAIL:
-    // also zero the rows past the end of the queries.
-    auto probs = [&](uint32_t b, int i0, auto tail) {
+    // Probabilities and ds of the tile at rows i0.. (in LDS at b), in three
+    // parts so that a step can spread them over its MFMAs: the row
+    // statistics and mask bounds, one element, the packing.  TAIL: also
+    // zero the rows past the end of the queries.
+    struct PStat {
+        float L[16], Dl[16];
+        int lim, rows;
+    };
+    auto pstats = [&](uint32_t b, int i0) {
+        PStat ps;
         // lse and delta of rows 8*hi + 0..7 and 16 + 8*hi + 0..7
         const float4 *lt4 = (const float4 *)(smem + b + 2 * TILEB) + 2 * hi;
         const float4 *dl4 = lt4 + BQ / 4;
-        float L[16], Dl[16];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const int src = (q4 & 1) + 4 * (q4 >> 1);
             const float4 a = lt4[src], d = dl4[src];
-            L[4 * q4] = a.x; L[4 * q4 + 1] = a.y; L[4 * q4 + 2] = a.z; L[4 * q4 + 3] = a.w;
-            Dl[4 * q4] = d.x; Dl[4 * q4 + 1] = d.y; Dl[4 * q4 + 2] = d.z; Dl[4 * q4 + 3] = d.w;
+            ps.L[4 * q4] = a.x; ps.L[4 * q4 + 1] = a.y; ps.L[4 * q4 + 2] = a.z; ps.L[4 * q4 + 3] = a.w;
+            ps.Dl[4 * q4] = d.x; ps.Dl[4 * q4 + 1] = d.y; ps.Dl[4 * q4 + 2] = d.z; ps.Dl[4 * q4 + 3] = d.w;
         }
         // causal: keep key kw + l32 for row i0 + row when row >= lim
         int lim = (CAUSAL && i0 < kw + 31) ? kw + l32 - i0 : -1;
@@ -485,24 +496,31 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
             if (p.wl >= 0) rows = min(rows, key_abs + p.wl + 1 - i0);
         }
         // element r is row 8*hi + c(r), c(r) = acc_row(r, 0) a constant
-        lim -= 8 * hi;
-        rows -= 8 * hi;
+        ps.lim = lim - 8 * hi;
+        ps.rows = rows - 8 * hi;
+        return ps;
+    };
+    auto pelem = [&](const PStat &ps, int r, const f32x16 &s, const f32x16 &dp, float (&pv)[16],
+                     float (&dsv)[16], auto tail) {
+        float e = exp2_fast(fmaf(s[r], p.c, -ps.L[r] * kLog2e));
+        if (CAUSAL || WIN) e = acc_row(r, 0) >= ps.lim ? e : 0.f;
+        if (decltype(tail)::value || WIN) e = acc_row(r, 0) < ps.rows ? e : 0.f;
+        pv[r] = e;
+        dsv[r] = e * (dp[r] - ps.Dl[r]);
+    };
+    auto ppack = [&](int h, int w, const float (&pv)[16], const float (&dsv)[16]) {
+        pk[h][w] = Ops::pack2(pv[8 * h + 2 * w], pv[8 * h + 2 * w + 1]);
+        dsk[h][w] = Ops::pack2(dsv[8 * h + 2 * w], dsv[8 * h + 2 * w + 1]);
+    };
+    auto probs = [&](uint32_t b, int i0, const f32x16 &s, const f32x16 &dp, auto tail) {
+        const PStat ps = pstats(b, i0);
         float pv[16], dsv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float e = exp2_fast(fmaf(s[r], p.c, -L[r] * kLog2e));
-            if (CAUSAL || WIN) e = acc_row(r, 0) >= lim ? e : 0.f;
-            if (decltype(tail)::value || WIN) e = acc_row(r, 0) < rows ? e : 0.f;
-            pv[r] = e;
-            dsv[r] = e * (dp[r] - Dl[r]);
-        }
+        for (int r = 0; r < 16; ++r) pelem(ps, r, s, dp, pv, dsv, tail);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                pk[h][w] = Ops::pack2(pv[8 * h + 2 * w], pv[8 * h + 2 * w + 1]);
-                dsk[h][w] = Ops::pack2(dsv[8 * h + 2 * w], dsv[8 * h + 2 * w + 1]);
-            }
+            for (int w = 0; w < 4; ++w) ppack(h, w, pv, dsv);
     };
     auto grads = [&](uint32_t b) {
         u32x4 tg[2][DB], tq[2][DB];
@@ -527,14 +545,81 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
     using no_tail = std::integral_constant<bool, false>;
     using with_tail = std::integral_constant<bool, true>;
 
-    // One step: tile t+3 requested, S/dP of tile t+1, dV/dK of tile t, the
-    // probabilities of tile t+1; then tile t+2 must have arrived.
-    auto step = [&](int t, auto tail) {
+    // One step: tile t+3 requested; S/dP of tile t+1 on the MFMA pipe while
+    // the vector ALU forms the probabilities and dS of tile t (from the S/dP
+    // of the previous step) and the transposing reads of the dV/dK operands
+    // of tile t go out; then dV/dK of tile t.  Tile t+2 must have arrived by
+    // the step's end.  The S/dP products are laid out one dimension chunk
+    // at a time with their share of the elements and reads, each chunk
+    // fenced from the next, so that the vector work fills the MFMA pipe's
+    // time instead of following it.
+    auto step = [&](int t) {
+        const int i0 = i_begin + t * BQ;
+        issue(i0 + 3 * BQ, buf(t + 3));
+        const f32x16 sc = s, dpc = dp;
+        const uint32_t bn = buf(t + 1), bc = buf(t);
+        // the row statistics first: LDS reads complete in order, and the
+        // first elements need them while the first products need only aq[0]
+        const PStat ps = pstats(bc, i0);
+        u32x4 aq[DC], ag[DC];
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+            aq[dc] = *(const u32x4 *)(smem + bn + rd_row[dc]);
+            ag[dc] = *(const u32x4 *)(smem + bn + TILEB + rd_row[dc]);
+        }
+        float pv[16], dsv[16];
+        u32x4 tg[2][DB], tq[2][DB];
+        constexpr int EPC = 16 / DC;          // elements per dimension chunk
+        constexpr int RPC = 2 * DB / DC;      // operand pairs read per chunk (>= 1)
+        static_assert(16 % DC == 0 && (2 * DB) % DC == 0 && RPC >= 1, "step split");
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+            if (dc == 0) {
+                s = Ops::mma(aq[0], kop[0], f32x16{});
+                dp = Ops::mma(ag[0], vop[0], f32x16{});
+            } else {
+                s = Ops::mma(aq[dc], kop[dc], s);
+                dp = Ops::mma(ag[dc], vop[dc], dp);
+            }
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) pelem(ps, dc * EPC + e, sc, dpc, pv, dsv, no_tail());
+#pragma unroll
+            for (int e = 0; e < EPC; e += 2) {
+                const int r = dc * EPC + e;   // elements r, r+1 complete a pair
+                ppack(r >> 3, (r & 7) >> 1, pv, dsv);
+            }
+#pragma unroll
+            for (int x = 0; x < RPC; ++x) {
+                const int idx = dc * RPC + x, kc = idx / DB, db = idx % DB;
+                const uint32_t co = (uint32_t)(kc * 16 * ROWB);
+                tg[kc][db] = read_tr<DB>(smem + bc + TILEB, rd_tr, db, co);
+                tq[kc][db] = read_tr<DB>(smem + bc, rd_tr, db, co);
+            }
+#if BWD_KV_SCHED
+            __builtin_amdgcn_sched_barrier(0);
+#endif
+        }
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                dv[db] = Ops::mma(tg[kc][db], pk[kc], dv[db]);
+                dk[db] = Ops::mma(tq[kc][db], dsk[kc], dk[db]);
+            }
+        wait_vmcnt<LPI>();
+        __syncthreads();
+    };
+
+    // The same step for two waves per SIMD (D = 64), where the partner wave
+    // hides what one wave leaves idle: tile t+3 requested, S/dP of tile t+1,
+    // dV/dK of tile t with the probabilities of tile t+1 between its
+    // products (pinned with sched_group_barrier).
+    auto step2 = [&](int t, auto tail) {
         const int i0 = i_begin + t * BQ;
         issue(i0 + 3 * BQ, buf(t + 3));
         sdp(buf(t + 1));
         grads(buf(t));
-        probs(buf(t + 1), i0 + BQ, tail);
+        probs(buf(t + 1), i0 + BQ, s, dp, tail);
 #if BWD_KV_SCHED
         // the loads first; the S/dP operands; the S/dP products with the
         // transposing reads of the dV/dK operands between them; the dV/dK
@@ -563,10 +648,15 @@ void fa_bwd_dkdv_mfma_kernel(BwdParams p)
         wait_vmcnt<LPI>();
         __syncthreads();
         sdp(buf(0));
-        probs(buf(0), i_begin, with_tail());
         int t = 0;
-        for (; t + 2 < ntiles; ++t) step(t, no_tail());
-        if (t + 1 < ntiles) step(t++, with_tail());
+        if constexpr (OCC == 1) {
+            for (; t + 1 < ntiles; ++t) step(t);
+            probs(buf(t), i_begin + t * BQ, s, dp, with_tail());
+        } else {
+            probs(buf(0), i_begin, s, dp, with_tail());
+            for (; t + 2 < ntiles; ++t) step2(t, no_tail());
+            if (t + 1 < ntiles) step2(t++, with_tail());
+        }
         grads(buf(t));
     }
     wait_vmcnt<0>();
