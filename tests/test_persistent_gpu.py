@@ -42,6 +42,8 @@ CASES = [
     (1, 128, 1024, 1024, "bf16", True, None),    # peaky: the stabiliser moves
     (1, 64, 2048, 640, "bf16", False, 0.5),      # large scale
     (1, 32, 4096, 4096, "f16", True, None),      # long rows, 2 blocks per workgroup
+    (8, 16, 1024, 4096, "f16", False, None),     # 32 tiles, 2 blocks per workgroup
+    (2, 64, 1000, 777, "bf16", False, None),     # ragged Lq and Lk, 13 tiles
 ]
 
 
