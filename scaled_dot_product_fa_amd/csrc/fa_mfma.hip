@@ -214,16 +214,30 @@ struct Params {
 
 // Workgroup id -> (head bh, query block qt).  Hardware places workgroup w
 // on XCD w % 8; consecutive logical ids are made to share an XCD.
+// `grouped` (causal calls with a left window edge): see below.
 __device__ __forceinline__ void decompose(int wg, int nwg, int BH, int ntq,
-                                          bool causal, int &bh, int &qt)
+                                          bool causal, int &bh, int &qt, bool grouped = false)
 {
     const int per = nwg >> 3, rem = nwg & 7;
     const int xcd = wg & 7, idx = wg >> 3;
     if (causal && (BH & 7) == 0) {
         // each XCD owns BH/8 heads; longest query blocks first
         const int hpx = BH >> 3;
-        qt = ntq - 1 - idx / hpx;
-        bh = xcd * hpx + idx % hpx;
+        // grouped: the heads g at a time (g: the fewest heads, dividing
+        // BH/8, whose blocks fill the XCD's 32 CUs), longest blocks of the
+        // group first, so that the blocks of few heads stream the same K/V
+        // tiles together.  It gains where the window keeps the blocks'
+        // work alike (+5% at 4096 rows with a 1024-key window) but loses a
+        // little on plain causal calls, whose longest-first order over all
+        // the XCD's heads balances better.
+        int g = hpx;
+        if (grouped) {
+            g = 1;
+            while (g < hpx && (g * ntq < 32 || hpx % g != 0)) ++g;
+        }
+        const int grp = idx / (g * ntq), r = idx % (g * ntq);
+        qt = ntq - 1 - r / g;
+        bh = xcd * hpx + grp * g + r % g;
         return;
     }
     const int logical = xcd < rem ? xcd * (per + 1) + idx
@@ -1088,7 +1102,7 @@ void fa_fwd_mfma_pp_kernel(Params p)
     const int hi = lane >> 5;
 
     int bh, qt;
-    decompose(blockIdx.x, gridDim.x, p.BH, p.ntq, CAUSAL, bh, qt);
+    decompose(blockIdx.x, gridDim.x, p.BH, p.ntq, CAUSAL, bh, qt, WIN && p.wl >= 0);
     const int q_first = qt * BM;
     const int qw = q_first + wave * 32;   // first query row of this wave
     const int qrow = qw + l32;            // this lane's query row
